@@ -1,0 +1,168 @@
+/*
+ * nf4.h -- C ABI of the MI355X (gfx950) NF4 weight codec and AQLoRA layer
+ * selector.
+ *
+ * What the calls compute, and where the pages define it:
+ *   - NF4: 4-bit NormalFloat, 16 values placed so that each gets an equal share
+ *     of normally distributed weights ("QLoRA" paper summary page,
+ *     ai360xpert.com, How It Works, NF4 item; "QLoRA Explained",
+ *     devtoolshub.net, section NF4).
+ *   - Quantisation constants and their double quantisation (same QLoRA page,
+ *     How It Works, Double Quantization item; "QLoRA Explained", section
+ *     Double Quantization).
+ *   - Dequantisation of every 4-bit weight back to 16-bit (QLoRA page, How It
+ *     Works; AQLoRA paper listing, arxivdaily.com, English abstract).
+ *   - AQLoRA's single pass: rank layers by NF4 reconstruction error and keep
+ *     the top-K in 16-bit under a memory budget, from the weights alone
+ *     (AQLoRA listing, English abstract; "AQLoRA: A Zero-Search Recipe for
+ *     Fast Quantized LoRA Fine-Tuning", aitrending.vip, Technical Details).
+ *
+ * Format (the readings taken where the pages are silent):
+ *   - blocks of 64 consecutive elements of the flattened row-major matrix
+ *     (the last block may be partial); constant = the block's largest |x| in
+ *     fp32 ("absmax");
+ *   - code of x = number of the 15 nearest-level thresholds strictly below
+ *     s = fl32(x * fl32(1/absmax)); ascending level order, code 7 = 0.0;
+ *     an all-zero block encodes to 7; blocks with absmax below 2^-126 are
+ *     scaled by 2^64 first (exact);
+ *   - codes packed two per byte, element 2j in the low nibble of byte j, an
+ *     odd final element leaves the high nibble 0;
+ *   - double quantisation (dq_group = 256): per matrix, groups of 256
+ *     consecutive absmax values; scale2 = fl32(G/127) with G the group's
+ *     largest absmax; qabsmax = rint(fl32(absmax/scale2)) as int8 (ties to
+ *     even); the dequantised constant is fl32(qabsmax * scale2).  Codes
+ *     always use the exact absmax;
+ *   - dequantised value = round-to-nearest-even to the input's 16-bit type of
+ *     fl32(level[code] * constant);
+ *   - reconstruction error of a matrix = sum over its elements of
+ *     (x - dequantised x)^2, accumulated in fp32 within a block of 64 and in
+ *     fp64 across blocks, in a fixed order (bitwise reproducible);
+ *   - promotion cost = 2n - NF4 bytes; ranking by error descending, equal
+ *     errors by index ascending; K = the longest prefix of that order whose
+ *     running cost stays within the budget (and within the count cap).
+ *
+ * Conventions for every call:
+ *   - Buffers named "device" are device pointers the caller allocated and
+ *     owns; the library never allocates or frees device memory and keeps no
+ *     pointer after it returns.  `stream` is a hipStream_t (NULL = the null
+ *     stream); calls only enqueue work on it and return -- the caller
+ *     synchronises.  Every device buffer must stay alive until that work is
+ *     done.  The nf4_layer array is host memory, copied into the workspace
+ *     before the call returns; the caller may reuse it at once.
+ *   - `ws` is caller-provided device scratch of at least the size the matching
+ *     *_workspace_bytes helper returns (256-byte aligned).  Calls on one stream
+ *     may share a workspace; concurrent calls on different streams need their
+ *     own.
+ *   - All argument checks run on the host before anything is enqueued; on an
+ *     error nothing is enqueued and no output is touched.  No call prints,
+ *     throws or aborts.  A failed HIP call returns NF4_E_HIP and its code is
+ *     kept per thread for nf4_last_hip_error().  Faults inside kernels surface
+ *     at the caller's next synchronisation.
+ *   - Inputs must be finite; NaN/Inf weights or errors give unspecified
+ *     (but memory-safe) results.
+ *   - Outputs are bitwise deterministic run to run.
+ */
+#ifndef NF4_H
+#define NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4_ABI_VERSION 1
+
+typedef enum {
+    NF4_OK = 0,
+    NF4_E_ARG = 1,          /* NULL where required, nl <= 0, n <= 0, sizes out of range   */
+    NF4_E_ALIGN = 2,        /* a pointer violates its alignment                           */
+    NF4_E_UNSUPPORTED = 3,  /* blocksize != 64, dq_group not in {0, 256}, bad dtype       */
+    NF4_E_WORKSPACE = 4,    /* ws NULL, misaligned, or ws_bytes too small                 */
+    NF4_E_HIP = 5           /* a HIP runtime call or launch failed                        */
+} nf4_status;
+
+typedef enum { NF4_BF16 = 0, NF4_FP16 = 1 } nf4_dtype;
+
+typedef struct {
+    int32_t dtype;      /* nf4_dtype of the 16-bit weights (and of dequantised output)  */
+    int32_t blocksize;  /* must be 64                                                   */
+    int32_t dq_group;   /* 0 = no double quantisation, 256 = int8 + fp32 per 256 blocks */
+} nf4_format;
+
+/* One weight matrix ("layer"), flattened row-major, n elements, nb = ceil(n/64)
+ * blocks, ng = ceil(nb/256) groups.  Which fields a call reads or writes is
+ * listed at each call; unused fields may be NULL. */
+typedef struct {
+    int64_t     n;        /* elements, 1 <= n < 2^40                                   */
+    const void* w;        /* device [n] 16-bit weights, 16-byte aligned                */
+    uint8_t*    codes;    /* device [ceil(n/2)] packed codes, 4-byte aligned           */
+    float*      absmax;   /* device [nb] exact fp32 block absmax, 4-byte aligned       */
+    int8_t*     qabsmax;  /* device [nb] int8 double-quantised absmax                  */
+    float*      scale2;   /* device [ng] fp32 second-level scales, 4-byte aligned      */
+    void*       out;      /* device [n] 16-bit dequantised output, 16-byte aligned     */
+} nf4_layer;
+
+/* Blockwise NF4 quantisation of nl matrices in one grouped launch.
+ * Reads w; writes codes and absmax; with dq_group == 256 also writes
+ * qabsmax and scale2 (double quantisation fused into the same pass).
+ * Required: w, codes, absmax; qabsmax and scale2 when dq_group == 256. */
+nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Double quantisation of existing absmax constants (dq_group must be 256).
+ * Reads absmax; writes qabsmax and scale2. */
+nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Dequantisation to the 16-bit type fmt.dtype.  Reads codes and either absmax
+ * (dq_group == 0) or qabsmax + scale2 (dq_group == 256); writes out.
+ * AQLoRA calls it for the layers that were not promoted. */
+nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The fused single pass: quantise (+ double-quantise), dequantise in
+ * registers with the constants the user gets back, and score each matrix.
+ * Reads w; writes codes, qabsmax and scale2 (dq_group == 256), absmax
+ * (required when dq_group == 0, optional -- NULL skips it -- when 256), and
+ * err[nl] (device fp64, the reconstruction error of each matrix).  out is not
+ * touched. */
+nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                           double* err, void* ws, size_t ws_bytes, void* stream);
+
+/* Budgeted top-K over per-layer scores, on the device.
+ *   err[nl]   device fp64 scores (finite, as written by nf4_layer_error)
+ *   cost[nl]  device int64 promotion costs (aqlora_promote_cost)
+ *   budget_bytes  < 0: no byte budget;  k_cap < 0: no count cap
+ *   selected[nl]  device uint8, 1 for promoted layers, 0 otherwise
+ *   k_out         device int32, K
+ * 1 <= nl <= 65536. */
+nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl,
+                              int64_t budget_bytes, int32_t k_cap,
+                              uint8_t* selected, int32_t* k_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---- host-only helpers (pure; no HIP calls) ---- */
+
+/* Workspace for every codec call above over these matrices; 0 on bad input. */
+size_t      nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format fmt);
+/* Workspace for aqlora_select_topk; 0 on bad input. */
+size_t      aqlora_workspace_bytes(int32_t nl);
+/* ceil(n/2) + (dq_group ? nb + 4*ng : 4*nb); -1 on bad input. */
+int64_t     nf4_storage_bytes(int64_t n, nf4_format fmt);
+/* 2n - nf4_storage_bytes(n, fmt): extra bytes of keeping the matrix 16-bit. */
+int64_t     aqlora_promote_cost(int64_t n, nf4_format fmt);
+/* The 16 NF4 levels in code order (ascending), as embedded in the kernels. */
+void        nf4_levels(float out16[16]);
+/* The 15 decision thresholds (fp32), as embedded in the kernels. */
+void        nf4_thresholds(float out15[15]);
+const char* nf4_status_str(nf4_status s);
+int32_t     nf4_abi_version(void);
+/* HIP error code (hipError_t value) of the last NF4_E_HIP on this thread. */
+int32_t     nf4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NF4_H */

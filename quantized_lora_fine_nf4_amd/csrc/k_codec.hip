@@ -1,0 +1,613 @@
+// k_codec.hip -- NF4 codec kernels for gfx950 (CDNA4, wave64).
+//
+// One tile = one double-quantisation group = 256 blocks of 64 weights
+// (16384 weights, 32 KB of bf16).  A 256-thread workgroup (4 waves) owns a
+// tile at a time and walks the flat tile index of all layers (one grouped,
+// persistent launch for the whole stack).  Lane layout: wave w, load j
+// (j = 0..7), lane L reads weights w*4096 + j*512 + 8L .. +8 with one 128-bit
+// load, so each load instruction of a wave covers 1 KB contiguously and the 8
+// lanes 8m..8m+7 hold the 64 weights of one block.
+//
+// What is computed (see nf4.h for the full format):
+//   absmax      -- "quantisation constants" per block ("QLoRA" paper summary
+//                  page, How It Works; "QLoRA Explained", Double Quantization)
+//   NF4 codes   -- nearest of the 16 quantile levels (QLoRA page, NF4 item)
+//   int8 DQ     -- the constants quantised again (QLoRA page, Double
+//                  Quantization item)
+//   dequant     -- back to 16-bit (QLoRA page, How It Works; AQLoRA listing,
+//                  English abstract)
+//   error       -- AQLoRA's per-layer NF4 reconstruction error (AQLoRA
+//                  listing, English abstract)
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4_format.h"
+#include "nf4_internal.h"
+
+namespace nf4k {
+namespace {
+
+constexpr int kWaves = kThreads / 64;                    // 4
+constexpr int kLoads = kTileElems / (kThreads * 8);      // 8 x 128-bit loads per lane
+constexpr int kCells = 129;                              // encode cells, trunc(64 s) in [-64, 64]
+constexpr int kRepl = 4;                                 // copies of the cell table (LDS banks)
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// One encode cell.  u = 64*s is cut into cells by truncation toward zero:
+// cell k > 0 holds u in [k, k+1), k < 0 holds (k-1, k], k = 0 holds (-1, 1).
+// The level gap (>= 0.0796, i.e. >= 5.09 in u) is wider than any cell's
+// closure, so at most one threshold lies in it:
+//   code = base + (u > thr),  thr = that threshold * 64 (or +inf),
+//   base = number of thresholds strictly below the cell.
+// u and thr are exact scalings by 64 of s and the fp32 threshold, so the
+// comparison is exactly "threshold < s".
+struct alignas(16) EncCell {
+    float thr;
+    uint32_t base;
+    float lv_lo;   // level[base]
+    float lv_hi;   // level[base + 1] (unused when thr is +inf)
+};
+
+__device__ void build_cells(EncCell* cells)
+{
+    for (int idx = threadIdx.x; idx < kCells * kRepl; idx += kThreads) {
+        const int k = idx / kRepl - 64;
+        const float lo = (k > 0) ? (float)k : (k < 0 ? (float)(k - 1) : -1.0f);
+        const float hi = (k > 0) ? (float)(k + 1) : (k < 0 ? (float)k : 1.0f);
+        uint32_t base = 0;
+        float thr = __builtin_inff();
+        for (int i = 0; i < 15; ++i) {
+            const float t64 = as_f(nf4fmt::kThresholdBits[i]) * 64.0f;
+            if (t64 < lo) ++base;
+            else if (t64 <= hi) thr = t64;
+        }
+        EncCell c;
+        c.thr = thr;
+        c.base = base;
+        c.lv_lo = as_f(nf4fmt::kLevelBits[base]);
+        c.lv_hi = as_f(nf4fmt::kLevelBits[base < 15 ? base + 1 : 15]);
+        cells[idx] = c;
+    }
+}
+
+// ---- 16-bit helpers ------------------------------------------------------
+
+// largest |x| bit pattern of 8 packed 16-bit values (sign-magnitude formats:
+// for non-negative values the integer order is the numeric order)
+__device__ __forceinline__ uint32_t absmax_bits8(const uint4 v)
+{
+    const uint32_t m = 0x7fff7fffu;
+    us2 a = __builtin_bit_cast(us2, v.x & m), b = __builtin_bit_cast(us2, v.y & m);
+    us2 c = __builtin_bit_cast(us2, v.z & m), d = __builtin_bit_cast(us2, v.w & m);
+    us2 r = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                      __builtin_elementwise_max(c, d));
+    return r.x > r.y ? (uint32_t)r.x : (uint32_t)r.y;
+}
+
+template <int DT>
+__device__ __forceinline__ float f16bits_to_f32(uint32_t h)
+{
+    if constexpr (DT == 0) return as_f(h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t d, float& lo, float& hi)
+{
+    if constexpr (DT == 0) {
+        lo = as_f(d << 16);
+        hi = as_f(d & 0xffff0000u);
+    } else {
+        lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(d & 0xffffu));
+        hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> 16));
+    }
+}
+
+// Keeps the compiler from fusing a product with the following conversion to
+// fp16 (v_fma_mix* rounds the exact product once; the format rounds to fp32
+// first and then to the 16-bit type).
+__device__ __forceinline__ float opaque(float x)
+{
+    __asm__ volatile("" : "+v"(x));
+    return x;
+}
+
+// Round two fp32 values to the 16-bit type (nearest, ties to even) and return
+// the packed pair; also the rounded values back in fp32.
+template <int DT>
+__device__ __forceinline__ uint32_t round_pair(float y0, float y1, float& r0, float& r1)
+{
+    if constexpr (DT == 0) {
+        f2 in = {y0, y1};
+        const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(in, bf2));
+        r0 = as_f(p << 16);
+        r1 = as_f(p & 0xffff0000u);
+        return p;
+    } else {
+        const _Float16 h0 = (_Float16)opaque(y0), h1 = (_Float16)opaque(y1);
+        r0 = (float)h0;
+        r1 = (float)h1;
+        return (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    }
+}
+
+// ---- cross-lane reductions -----------------------------------------------
+
+// Reduce over the 8 lanes of a block (lanes 8m..8m+7): pairs (i, 7-i), then
+// xor 1, then xor 2.  Every lane of the 8 ends with the same value, and the
+// order of the additions is fixed.
+__device__ __forceinline__ uint32_t max8_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
+__device__ __forceinline__ float sum8_f32(float v)
+{
+    v += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), 0x141, 0xF, 0xF, true));
+    v += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), 0xB1, 0xF, 0xF, true));
+    v += as_f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u(v), 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// ---- tile walk ---------------------------------------------------------
+
+struct TileRef {
+    const LayerDesc* d;
+    int64_t local;   // tile index within the layer
+    int64_t e0;      // first element of the tile within the layer
+    int valid;       // elements of the tile inside the layer (1..16384)
+};
+
+__device__ __forceinline__ int first_layer(const LayerDesc* tab, int nl, int64_t tile)
+{
+    int lo = 0, hi = nl - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (tab[mid].tile_end > tile) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_t tile)
+{
+    while (tab[l].tile_end <= tile) ++l;
+    TileRef r;
+    r.d = &tab[l];
+    const int64_t n = r.d->n;
+    r.local = tile - (r.d->tile_end - tiles_of(n));
+    r.e0 = r.local << kTileShift;
+    const int64_t rem = n - r.e0;
+    r.valid = rem < kTileElems ? (int)rem : kTileElems;
+    return r;
+}
+
+// ---- fused quantise / double-quantise / dequantise / error --------------
+
+struct CodecShared {
+    EncCell cells[kCells * kRepl];
+    uint32_t amax[256];      // block absmax bits (16-bit pattern)
+    f2 blk[256];             // per block: (64 / absmax [scaled], dequantised absmax)
+    float pre[256];          // per block: 2^64 when absmax < 2^-100, else 1
+    int escale[256];         // per block: k with absmax * 2^k in [1, 2) for extreme absmax, else 0
+    uint32_t wmax[kWaves];
+    double wsum[kWaves];
+};
+
+// Step 4 of a tile for one lane: encode, pack and store the codes of its 64
+// weights; with ERR also dequantise them in registers and add up the squared
+// differences (fp32 over the 64 weights of a block, fp64 across blocks).
+// SPEC is the rare wave-uniform path for blocks with extreme absmax: the
+// weights are scaled by 2^64 before normalising (absmax < 2^-100, keeps 64/a
+// finite and leaves the codes unchanged), and each difference is scaled by
+// 2^k before squaring so that the fp32 squares neither underflow nor
+// overflow (exact; undone in fp64).
+template <int DT, bool ERR, bool FULL, bool SPEC>
+__device__ __forceinline__ double encode_lane(const CodecShared& sh, const uint4 (&v)[kLoads],
+                                              uint8_t* __restrict__ cp, int valid)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const EncCell* cells = sh.cells + (lane & (kRepl - 1));
+    double acc64 = 0.0;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int o = wv * 4096 + j * 512 + lane * 8;
+        const int bidx = wv * 64 + j * 8 + (lane >> 3);
+        const f2 bk = sh.blk[bidx];
+        float scale = 1.0f;
+        int ek = 0;
+        if constexpr (SPEC) {
+            scale = sh.pre[bidx];
+            ek = sh.escale[bidx];
+        }
+        const uint32_t dw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t pk = 0;
+        float e = 0.0f;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+            float x0, x1;
+            unpack2<DT>(dw[k2], x0, x1);
+            const float u0 = (SPEC ? x0 * scale : x0) * bk.x;
+            const float u1 = (SPEC ? x1 * scale : x1) * bk.x;
+            const EncCell c0 = cells[((int)u0 + 64) * kRepl];
+            const EncCell c1 = cells[((int)u1 + 64) * kRepl];
+            const bool h0 = u0 > c0.thr, h1 = u1 > c1.thr;
+            uint32_t code0 = c0.base + (h0 ? 1u : 0u);
+            uint32_t code1 = c1.base + (h1 ? 1u : 0u);
+            if constexpr (ERR) {
+                const float y0 = (h0 ? c0.lv_hi : c0.lv_lo) * bk.y;
+                const float y1 = (h1 ? c1.lv_hi : c1.lv_lo) * bk.y;
+                float r0, r1;
+                (void)round_pair<DT>(y0, y1, r0, r1);
+                float d0 = x0 - r0, d1 = x1 - r1;
+                if constexpr (SPEC) {
+                    d0 = __builtin_amdgcn_ldexpf(d0, ek);
+                    d1 = __builtin_amdgcn_ldexpf(d1, ek);
+                }
+                e = __builtin_fmaf(d0, d0, e);
+                e = __builtin_fmaf(d1, d1, e);
+            }
+            if constexpr (!FULL) {
+                if (o + 2 * k2 >= valid) code0 = 0;
+                if (o + 2 * k2 + 1 >= valid) code1 = 0;
+            }
+            pk |= (code0 << (8 * k2)) | (code1 << (8 * k2 + 4));
+        }
+        if constexpr (FULL) {
+            *(uint32_t*)(cp + (o >> 1)) = pk;
+        } else {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                if (o + 2 * bb < valid) cp[(o >> 1) + bb] = (uint8_t)(pk >> (8 * bb));
+        }
+        if constexpr (ERR) {
+            const double blk_sse = (double)sum8_f32(e);
+            acc64 += SPEC ? __builtin_ldexp(blk_sse, -2 * ek) : blk_sse;
+        }
+    }
+    return acc64;
+}
+
+template <int DT, bool DQ, bool ERR, bool FULL>
+__device__ __forceinline__ void codec_tile(CodecShared& sh, const TileRef& tr, int64_t tile,
+                                           double* __restrict__ partial)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const LayerDesc& d = *tr.d;
+    const uint16_t* __restrict__ w = (const uint16_t*)d.w + tr.e0;
+    const int valid = tr.valid;
+
+    // 1. 128-bit loads, 8 per lane (the whole tile in registers)
+    uint4 v[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int o = wv * 4096 + j * 512 + lane * 8;
+        if constexpr (FULL) {
+            v[j] = *(const uint4*)(w + o);
+        } else {
+            uint16_t h[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = (o + k < valid) ? w[o + k] : (uint16_t)0;
+            v[j].x = h[0] | ((uint32_t)h[1] << 16);
+            v[j].y = h[2] | ((uint32_t)h[3] << 16);
+            v[j].z = h[4] | ((uint32_t)h[5] << 16);
+            v[j].w = h[6] | ((uint32_t)h[7] << 16);
+        }
+    }
+
+    // 2. block absmax (exact: a max of representable values)
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const uint32_t m = max8_u32(absmax_bits8(v[j]));
+        if ((lane & 7) == 0) sh.amax[wv * 64 + j * 8 + (lane >> 3)] = m;
+    }
+    __syncthreads();
+
+    // 3. per-block constants, thread t owns block t of the tile
+    const float a = f16bits_to_f32<DT>(sh.amax[t]);
+    float adq = a;
+    int8_t q = 0;
+    float s2 = 0.0f;
+    if constexpr (DQ) {
+        const uint32_t wm = wave_max_u32(as_u(a));
+        if (lane == 0) sh.wmax[wv] = wm;
+        __syncthreads();
+        uint32_t g = sh.wmax[0];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) g = max(g, sh.wmax[i]);
+        const float G = as_f(g);
+        if (G > 0.0f) {
+            s2 = G / 127.0f;
+            float qf = rintf(a / s2);
+            qf = fminf(fmaxf(qf, -127.0f), 127.0f);
+            q = (int8_t)qf;
+            adq = (float)q * s2;
+        } else {
+            adq = 0.0f;
+        }
+    }
+    // normalisation s = fl32(x * fl32(1/a)); carried as u = 64 s = x * (64/a)
+    float r64 = 0.0f, pre = 1.0f;
+    int ek = 0;
+    if (a > 0.0f) {
+        if (a < 0x1p-100f) {   // keeps 64/a finite; for normal a the codes are unchanged
+            pre = 0x1p64f;
+            r64 = (1.0f / (a * 0x1p64f)) * 64.0f;
+        } else {
+            r64 = (1.0f / a) * 64.0f;
+        }
+        if (ERR && (a < 0x1p-40f || a >= 0x1p40f)) ek = 1 - __builtin_amdgcn_frexp_expf(a);
+    }
+    sh.blk[t] = f2{r64, adq};
+    sh.pre[t] = pre;
+    sh.escale[t] = ek;
+    {
+        const int nbv = (valid + 63) >> 6;
+        const int64_t b = (tr.e0 >> 6) + t;
+        if (t < nbv) {
+            if (d.absmax) d.absmax[b] = a;
+            if constexpr (DQ) d.qabsmax[b] = q;
+        }
+        if constexpr (DQ) {
+            if (t == 0) d.scale2[tr.local] = s2;
+        }
+    }
+    const int any_spec = __syncthreads_or(pre != 1.0f || ek != 0);
+
+    // 4. encode, pack, store codes; dequantise in registers and square the error
+    uint8_t* __restrict__ cp = d.codes + (tr.e0 >> 1);
+    const double acc = any_spec ? encode_lane<DT, ERR, FULL, true>(sh, v, cp, valid)
+                                : encode_lane<DT, ERR, FULL, false>(sh, v, cp, valid);
+
+    if constexpr (ERR) {
+        // lanes of one block group hold the same sum; add the 8 groups in a fixed tree
+        double acc64 = acc;
+        acc64 += __shfl_xor(acc64, 8, 64);
+        acc64 += __shfl_xor(acc64, 16, 64);
+        acc64 += __shfl_xor(acc64, 32, 64);
+        if (lane == 0) sh.wsum[wv] = acc64;
+        __syncthreads();
+        if (t == 0) partial[tile] = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
+    }
+}
+
+template <int DT, bool DQ, bool ERR>
+__global__ __launch_bounds__(kThreads) void k_codec(const LayerDesc* __restrict__ tab, int nl,
+                                                    int64_t ntiles, double* __restrict__ partial)
+{
+    __shared__ CodecShared sh;
+    build_cells(sh.cells);
+    __syncthreads();
+    if ((int64_t)blockIdx.x >= ntiles) return;
+    int l = first_layer(tab, nl, blockIdx.x);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const TileRef tr = tile_ref(tab, l, tile);
+        if (tr.valid == kTileElems) codec_tile<DT, DQ, ERR, true>(sh, tr, tile, partial);
+        else                        codec_tile<DT, DQ, ERR, false>(sh, tr, tile, partial);
+    }
+}
+
+// ---- standalone dequantisation -------------------------------------------
+
+template <int DT, bool DQ, bool FULL>
+__device__ __forceinline__ void dequant_tile(const float* s_lv, const TileRef& tr)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const LayerDesc& d = *tr.d;
+    const int valid = tr.valid;
+    const uint8_t* __restrict__ cp = d.codes + (tr.e0 >> 1);
+    uint16_t* __restrict__ outp = (uint16_t*)d.out + tr.e0;
+    const int64_t b0 = tr.e0 >> 6;
+    const float s2 = DQ ? d.scale2[tr.local] : 0.0f;
+
+    uint32_t c32[kLoads];
+    float adq[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int o = wv * 4096 + j * 512 + lane * 8;
+        const int64_t b = b0 + (o >> 6);
+        if constexpr (FULL) {
+            c32[j] = *(const uint32_t*)(cp + (o >> 1));
+        } else {
+            uint32_t c = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                if (o + 2 * bb < valid) c |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
+            c32[j] = c;
+        }
+        if (FULL || o < valid) {
+            if constexpr (DQ) adq[j] = (float)d.qabsmax[b] * s2;
+            else              adq[j] = d.absmax[b];
+        } else {
+            adq[j] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int o = wv * 4096 + j * 512 + lane * 8;
+        uint32_t p[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+            const float y0 = s_lv[(c32[j] >> (8 * k2)) & 15] * adq[j];
+            const float y1 = s_lv[(c32[j] >> (8 * k2 + 4)) & 15] * adq[j];
+            float r0, r1;
+            p[k2] = round_pair<DT>(y0, y1, r0, r1);
+        }
+        if constexpr (FULL) {
+            *(uint4*)(outp + o) = uint4{p[0], p[1], p[2], p[3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (o + k < valid) outp[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
+        }
+    }
+}
+
+template <int DT, bool DQ>
+__global__ __launch_bounds__(kThreads) void k_dequant(const LayerDesc* __restrict__ tab, int nl,
+                                                      int64_t ntiles)
+{
+    __shared__ float s_lv[16];
+    if (threadIdx.x < 16) s_lv[threadIdx.x] = as_f(nf4fmt::kLevelBits[threadIdx.x]);
+    __syncthreads();
+    if ((int64_t)blockIdx.x >= ntiles) return;
+    int l = first_layer(tab, nl, blockIdx.x);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const TileRef tr = tile_ref(tab, l, tile);
+        if (tr.valid == kTileElems) dequant_tile<DT, DQ, true>(s_lv, tr);
+        else                        dequant_tile<DT, DQ, false>(s_lv, tr);
+    }
+}
+
+// ---- standalone double quantisation --------------------------------------
+
+__global__ __launch_bounds__(kThreads) void k_double_quant(const LayerDesc* __restrict__ tab,
+                                                           int nl, int64_t ntiles)
+{
+    __shared__ uint32_t s_wmax[kWaves];
+    if ((int64_t)blockIdx.x >= ntiles) return;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    int l = first_layer(tab, nl, blockIdx.x);
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const TileRef tr = tile_ref(tab, l, tile);
+        const LayerDesc& d = *tr.d;
+        const int nbv = (tr.valid + 63) >> 6;
+        const int64_t b = (tr.e0 >> 6) + t;
+        const float a = (t < nbv) ? d.absmax[b] : 0.0f;
+        const uint32_t wm = wave_max_u32(as_u(a));
+        if (lane == 0) s_wmax[wv] = wm;
+        __syncthreads();
+        uint32_t g = s_wmax[0];
+        for (int i = 1; i < kWaves; ++i) g = max(g, s_wmax[i]);
+        __syncthreads();
+        const float G = as_f(g);
+        float s2 = 0.0f;
+        int8_t q = 0;
+        if (G > 0.0f) {
+            s2 = G / 127.0f;
+            float qf = rintf(a / s2);
+            qf = fminf(fmaxf(qf, -127.0f), 127.0f);
+            q = (int8_t)qf;
+        }
+        if (t < nbv) d.qabsmax[b] = q;
+        if (t == 0) d.scale2[tr.local] = s2;
+    }
+}
+
+// ---- per-layer reduction of the tile partials -----------------------------
+
+__global__ __launch_bounds__(kThreads) void k_reduce(const LayerDesc* __restrict__ tab,
+                                                     const double* __restrict__ partial,
+                                                     double* __restrict__ err)
+{
+    __shared__ double s[kThreads];
+    const int l = blockIdx.x, t = threadIdx.x;
+    const int64_t end = tab[l].tile_end;
+    const int64_t begin = end - tiles_of(tab[l].n);
+    double acc = 0.0;
+    for (int64_t i = begin + t; i < end; i += kThreads) acc += partial[i];
+    s[t] = acc;
+    __syncthreads();
+    for (int h = kThreads / 2; h >= 1; h >>= 1) {
+        if (t < h) s[t] = s[t] + s[t + h];
+        __syncthreads();
+    }
+    if (t == 0) err[l] = s[0];
+}
+
+// ---- launch helpers -------------------------------------------------------
+
+int cu_count()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+template <typename K>
+int64_t persistent_grid(K kernel, int64_t ntiles)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 4;
+    const int64_t g = (int64_t)cu_count() * per_cu;
+    return ntiles < g ? ntiles : g;
+}
+
+template <int DT, bool DQ, bool ERR>
+hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, double* partial, hipStream_t s)
+{
+    auto k = k_codec<DT, DQ, ERR>;
+    const int64_t grid = persistent_grid(k, ntiles);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, tab, nl, ntiles, partial);
+    return hipGetLastError();
+}
+
+template <int DT, bool DQ>
+hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)
+{
+    auto k = k_dequant<DT, DQ>;
+    const int64_t grid = persistent_grid(k, ntiles);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, tab, nl, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
+                        double* err_partial, hipStream_t s)
+{
+    const bool err = err_partial != nullptr;
+    if (dtype == 0) {
+        if (dq) return err ? codec_go<0, true, true>(tab, nl, ntiles, err_partial, s)
+                           : codec_go<0, true, false>(tab, nl, ntiles, nullptr, s);
+        return err ? codec_go<0, false, true>(tab, nl, ntiles, err_partial, s)
+                   : codec_go<0, false, false>(tab, nl, ntiles, nullptr, s);
+    }
+    if (dq) return err ? codec_go<1, true, true>(tab, nl, ntiles, err_partial, s)
+                       : codec_go<1, true, false>(tab, nl, ntiles, nullptr, s);
+    return err ? codec_go<1, false, true>(tab, nl, ntiles, err_partial, s)
+               : codec_go<1, false, false>(tab, nl, ntiles, nullptr, s);
+}
+
+hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
+                         hipStream_t s)
+{
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)nl), dim3(kThreads), 0, s, tab, partial, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
+                          hipStream_t s)
+{
+    if (dtype == 0) return dq ? dequant_go<0, true>(tab, nl, ntiles, s)
+                              : dequant_go<0, false>(tab, nl, ntiles, s);
+    return dq ? dequant_go<1, true>(tab, nl, ntiles, s) : dequant_go<1, false>(tab, nl, ntiles, s);
+}
+
+hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)
+{
+    const int64_t grid = persistent_grid(k_double_quant, ntiles);
+    hipLaunchKernelGGL(k_double_quant, dim3((unsigned)grid), dim3(kThreads), 0, s, tab, nl, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace nf4k

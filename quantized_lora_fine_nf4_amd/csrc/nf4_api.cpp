@@ -1,0 +1,252 @@
+// nf4_api.cpp -- the C entry points of include/nf4.h: argument validation
+// (all on the host, before anything is enqueued), workspace layout, staging
+// of the layer table, and the kernel launches.
+#include "nf4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <vector>
+
+#include "nf4_format.h"
+#include "nf4_internal.h"
+
+using nf4k::LayerDesc;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+constexpr int64_t kMaxN = int64_t(1) << 40;
+constexpr int32_t kMaxLayers = 1 << 24;
+constexpr int32_t kMaxSelectLayers = 65536;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nf4_status check_format(const nf4_format& f)
+{
+    if (f.blocksize != nf4fmt::kBlock) return NF4_E_UNSUPPORTED;
+    if (f.dq_group != 0 && f.dq_group != nf4fmt::kGroup) return NF4_E_UNSUPPORTED;
+    if (f.dtype != NF4_BF16 && f.dtype != NF4_FP16) return NF4_E_UNSUPPORTED;
+    return NF4_OK;
+}
+
+// Which pointers of a layer a call needs.
+enum Need : unsigned {
+    NEED_W = 1, NEED_CODES = 2, NEED_ABSMAX = 4, NEED_Q = 8, NEED_S2 = 16, NEED_OUT = 32,
+    OPT_ABSMAX = 64
+};
+
+nf4_status check_layers(const nf4_layer* L, int32_t nl, unsigned need, int64_t* ntiles_out)
+{
+    if (!L || nl <= 0 || nl > kMaxLayers) return NF4_E_ARG;
+    int64_t ntiles = 0;
+    for (int32_t i = 0; i < nl; ++i) {
+        const nf4_layer& x = L[i];
+        if (x.n <= 0 || x.n >= kMaxN) return NF4_E_ARG;
+        if ((need & NEED_W) && !x.w) return NF4_E_ARG;
+        if ((need & NEED_CODES) && !x.codes) return NF4_E_ARG;
+        if ((need & NEED_ABSMAX) && !x.absmax) return NF4_E_ARG;
+        if ((need & NEED_Q) && !x.qabsmax) return NF4_E_ARG;
+        if ((need & NEED_S2) && !x.scale2) return NF4_E_ARG;
+        if ((need & NEED_OUT) && !x.out) return NF4_E_ARG;
+        if ((need & NEED_W) && !aligned(x.w, 16)) return NF4_E_ALIGN;
+        if ((need & NEED_CODES) && !aligned(x.codes, 4)) return NF4_E_ALIGN;
+        if ((need & (NEED_ABSMAX | OPT_ABSMAX)) && x.absmax && !aligned(x.absmax, 4)) return NF4_E_ALIGN;
+        if ((need & NEED_S2) && !aligned(x.scale2, 4)) return NF4_E_ALIGN;
+        if ((need & NEED_OUT) && !aligned(x.out, 16)) return NF4_E_ALIGN;
+        ntiles += nf4k::tiles_of(x.n);
+    }
+    *ntiles_out = ntiles;
+    return NF4_OK;
+}
+
+size_t table_bytes(int32_t nl) { return align256(size_t(nl) * sizeof(LayerDesc)); }
+size_t partial_bytes(int64_t ntiles) { return align256(size_t(ntiles) * sizeof(double)); }
+
+nf4_status check_ws(const void* ws, size_t ws_bytes, size_t need)
+{
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return NF4_E_WORKSPACE;
+    return NF4_OK;
+}
+
+nf4_status hip_fail(hipError_t e)
+{
+    g_last_hip = static_cast<int32_t>(e);
+    return NF4_E_HIP;
+}
+
+// Build the device layer table in host memory and copy it into the workspace
+// on the stream.  The copy is from pageable memory, which the runtime stages
+// before the call returns, so the host vector may die right after.
+nf4_status stage_table(const nf4_layer* L, int32_t nl, void* ws, hipStream_t s)
+{
+    std::vector<LayerDesc> tab(static_cast<size_t>(nl));
+    int64_t run = 0;
+    for (int32_t i = 0; i < nl; ++i) {
+        run += nf4k::tiles_of(L[i].n);
+        tab[i] = LayerDesc{L[i].w, L[i].codes, L[i].absmax, L[i].qabsmax, L[i].scale2, L[i].out,
+                           L[i].n, run};
+    }
+    hipError_t e = hipMemcpyAsync(ws, tab.data(), sizeof(LayerDesc) * size_t(nl),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nf4_abi_version(void) { return NF4_ABI_VERSION; }
+int32_t nf4_last_hip_error(void) { return g_last_hip; }
+
+const char* nf4_status_str(nf4_status s)
+{
+    switch (s) {
+        case NF4_OK: return "ok";
+        case NF4_E_ARG: return "invalid argument";
+        case NF4_E_ALIGN: return "misaligned pointer";
+        case NF4_E_UNSUPPORTED: return "unsupported format";
+        case NF4_E_WORKSPACE: return "workspace missing, misaligned or too small";
+        case NF4_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+void nf4_levels(float out16[16])
+{
+    for (int i = 0; i < 16; ++i) std::memcpy(&out16[i], &nf4fmt::kLevelBits[i], 4);
+}
+
+void nf4_thresholds(float out15[15])
+{
+    for (int i = 0; i < 15; ++i) std::memcpy(&out15[i], &nf4fmt::kThresholdBits[i], 4);
+}
+
+int64_t nf4_storage_bytes(int64_t n, nf4_format f)
+{
+    if (n <= 0 || n >= kMaxN || check_format(f) != NF4_OK) return -1;
+    const int64_t nb = (n + nf4fmt::kBlock - 1) / nf4fmt::kBlock;
+    const int64_t ng = (nb + nf4fmt::kGroup - 1) / nf4fmt::kGroup;
+    return (n + 1) / 2 + (f.dq_group ? nb + 4 * ng : 4 * nb);
+}
+
+int64_t aqlora_promote_cost(int64_t n, nf4_format f)
+{
+    const int64_t s = nf4_storage_bytes(n, f);
+    return s < 0 ? -1 : 2 * n - s;
+}
+
+size_t nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format f)
+{
+    if (!n_per_layer || nl <= 0 || nl > kMaxLayers || check_format(f) != NF4_OK) return 0;
+    int64_t ntiles = 0;
+    for (int32_t i = 0; i < nl; ++i) {
+        if (n_per_layer[i] <= 0 || n_per_layer[i] >= kMaxN) return 0;
+        ntiles += nf4k::tiles_of(n_per_layer[i]);
+    }
+    return table_bytes(nl) + partial_bytes(ntiles);
+}
+
+size_t aqlora_workspace_bytes(int32_t nl)
+{
+    if (nl <= 0 || nl > kMaxSelectLayers) return 0;
+    return 2 * align256(size_t(nl) * sizeof(int32_t));
+}
+
+nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
+                        size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    const bool dq = fmt.dq_group != 0;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl, NEED_W | NEED_CODES | NEED_ABSMAX | (dq ? NEED_Q | NEED_S2 : 0u),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
+    hipError_t e = nf4k::launch_codec(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype, dq,
+                                      nullptr, s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
+                            size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    if (fmt.dq_group != nf4fmt::kGroup) return NF4_E_UNSUPPORTED;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl, NEED_ABSMAX | NEED_Q | NEED_S2, &ntiles);
+    if (st != NF4_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
+    hipError_t e = nf4k::launch_double_quant(static_cast<const LayerDesc*>(ws), nl, ntiles, s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
+                          size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    const bool dq = fmt.dq_group != 0;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl, NEED_CODES | NEED_OUT | (dq ? NEED_Q | NEED_S2 : NEED_ABSMAX),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
+    hipError_t e = nf4k::launch_dequant(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype,
+                                        dq, s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
+                           void* ws, size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    const bool dq = fmt.dq_group != 0;
+    if (!err) return NF4_E_ARG;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl,
+                      NEED_W | NEED_CODES | (dq ? NEED_Q | NEED_S2 | OPT_ABSMAX : NEED_ABSMAX),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if (!aligned(err, 8)) return NF4_E_ALIGN;
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + partial_bytes(ntiles))) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
+    const LayerDesc* tab = static_cast<const LayerDesc*>(ws);
+    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + table_bytes(nl));
+    hipError_t e = nf4k::launch_codec(tab, nl, ntiles, fmt.dtype, dq, partial, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = nf4k::launch_reduce(tab, nl, partial, err, s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl,
+                              int64_t budget_bytes, int32_t k_cap, uint8_t* selected,
+                              int32_t* k_out, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!err || !cost || !selected || !k_out) return NF4_E_ARG;
+    if (nl <= 0 || nl > kMaxSelectLayers) return NF4_E_ARG;
+    if (!aligned(err, 8) || !aligned(cost, 8) || !aligned(k_out, 4)) return NF4_E_ALIGN;
+    nf4_status st = check_ws(ws, ws_bytes, aqlora_workspace_bytes(nl));
+    if (st != NF4_OK) return st;
+    int32_t* rank = static_cast<int32_t*>(ws);
+    int32_t* perm = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                               align256(size_t(nl) * sizeof(int32_t)));
+    hipError_t e = nf4k::launch_select(err, cost, nl, budget_bytes, k_cap, selected, k_out, rank,
+                                       perm, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+}  // extern "C"

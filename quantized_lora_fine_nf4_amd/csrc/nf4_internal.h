@@ -1,0 +1,48 @@
+// nf4_internal.h -- device-side layer table and kernel launchers (not part of
+// the public ABI; the C entry points in nf4_api.cpp validate and call these).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4k {
+
+// One tile = one double-quantisation group = 256 blocks of 64 elements.
+constexpr int kTileElems = 16384;
+constexpr int kTileShift = 14;
+constexpr int kThreads = 256;
+
+// Device copy of one nf4_layer plus the running tile count: tiles of all
+// layers form one flat index space, layer l owning [tile_end - tiles(n), tile_end).
+struct LayerDesc {
+    const void* w;
+    uint8_t* codes;
+    float* absmax;
+    int8_t* qabsmax;
+    float* scale2;
+    void* out;
+    int64_t n;
+    int64_t tile_end;
+};
+static_assert(sizeof(LayerDesc) == 64, "layer table entry is 64 bytes");
+
+__host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileElems - 1) >> kTileShift; }
+
+// Fused blockwise quantisation (+ int8 double quantisation when dq) and, when
+// err_partial != nullptr, in-register dequantisation and per-tile fp64 squared
+// error written to err_partial[tile].
+hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
+                        double* err_partial, hipStream_t s);
+// Per-layer fixed-order sum of the per-tile partials into err[nl].
+hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
+                         hipStream_t s);
+// Standalone dequantisation (qabsmax/scale2 when dq, else absmax).
+hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
+                          hipStream_t s);
+// Standalone double quantisation of absmax.
+hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s);
+// Budgeted top-K; rank/perm are int32[nl] workspace arrays.
+hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,
+                         int kcap, uint8_t* selected, int32_t* k_out, int32_t* rank,
+                         int32_t* perm, hipStream_t s);
+
+}  // namespace nf4k

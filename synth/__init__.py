@@ -108,3 +108,32 @@ def generate_raw(seed: int, n: int, dtype: int = BF16, dist: int = NORMAL,
                               dtype, 0, n, out.ctypes.data, threads)
     assert rc == 0
     return out
+
+
+def fill_device(cfg: StackConfig, views, threads: int | None = None,
+                staging_elems: int = 1 << 26, progress=None) -> None:
+    """Generate every layer of ``cfg`` on the host and copy it into the
+    matching device tensor of ``views`` (int16 bit patterns, one per layer),
+    through two pinned staging buffers so generation overlaps the copies."""
+    import torch
+    bufs = [torch.empty(staging_elems, dtype=torch.int16, pin_memory=True) for _ in range(2)]
+    events = [None, None]
+    stream = torch.cuda.current_stream()
+    k = 0
+    for i in range(cfg.n_layers):
+        n = cfg.n(i)
+        assert views[i].numel() == n and views[i].dtype == torch.int16
+        for first in range(0, n, staging_elems):
+            cnt = min(staging_elems, n - first)
+            b = k % 2
+            if events[b] is not None:
+                events[b].synchronize()
+            generate_into(cfg, i, bufs[b].data_ptr(), first, cnt, threads)
+            views[i][first:first + cnt].copy_(bufs[b][:cnt], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            events[b] = ev
+            k += 1
+        if progress is not None:
+            progress(i)
+    torch.cuda.synchronize()

@@ -1,0 +1,173 @@
+"""C ABI contract on the host: symbols, helpers, argument errors (no GPU needed).
+
+Every argument check runs before any HIP call, so the error paths are
+exercised here with stand-in (never dereferenced) pointers.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_lora_fine_nf4_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-aligned stand-in address; no call below reaches the device
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "nf4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("nf4_", "aqlora_"))))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 14, names
+    L = ctypes.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q.EXPORTS), set(names) ^ set(q.EXPORTS)
+    assert q.nf4_abi_version() == 1
+
+
+def test_embedded_levels_and_thresholds_equal_the_oracles():
+    assert np.array_equal(q.nf4_levels().view(np.uint32), oracle.levels().view(np.uint32))
+    assert np.array_equal(q.nf4_thresholds().view(np.uint32), oracle.thresholds().view(np.uint32))
+
+
+def test_storage_and_cost_helpers_match_oracle():
+    rng = np.random.default_rng(0)
+    ns = [1, 2, 63, 64, 65, 127, 16383, 16384, 16385, 64 * 257, 4096 * 4096, 70_778_880]
+    ns += list(rng.integers(1, 10**9, 50))
+    for n in ns:
+        for dq in (False, True):
+            f = q.fmt(q.NF4_BF16, dq)
+            assert q.nf4_storage_bytes(int(n), f) == oracle.storage_bytes(int(n), dq)
+            assert q.aqlora_promote_cost(int(n), f) == oracle.promote_cost(int(n), dq)
+    assert q.nf4_storage_bytes(0, q.fmt()) == -1
+    assert q.nf4_storage_bytes(10, q.nf4_format(0, 32, 0)) == -1
+
+
+def test_workspace_sizes():
+    f = q.fmt()
+    ns = [16384 * 3 + 1, 100, 64]
+    tiles = 4 + 1 + 1
+    assert q.nf4_workspace_bytes(ns, f) == 256 + ((tiles * 8 + 255) // 256) * 256
+    assert q.nf4_workspace_bytes([], f) == 0
+    assert q.nf4_workspace_bytes([0], f) == 0
+    assert q.aqlora_workspace_bytes(280) == 2 * 1280
+    assert q.aqlora_workspace_bytes(0) == 0
+    assert q.aqlora_workspace_bytes(65537) == 0
+
+
+def _L(n=128, w=FAKE, codes=FAKE, absmax=FAKE, qabsmax=FAKE, scale2=FAKE, out=FAKE):
+    return q.nf4_layer(n, w, codes, absmax, qabsmax, scale2, out)
+
+
+def _call(name, layers, f, ws=FAKE, ws_bytes=1 << 20, err=FAKE):
+    L = q.lib()
+    arr = (q.nf4_layer * max(1, len(layers)))(*layers)
+    if name == "nf4_layer_error":
+        return L.nf4_layer_error(arr, len(layers), f, err, ws, ws_bytes, None)
+    return getattr(L, name)(arr, len(layers), f, ws, ws_bytes, None)
+
+
+CODEC = ["nf4_quantize", "nf4_double_quant", "nf4_dequantize", "nf4_layer_error"]
+
+
+@pytest.mark.parametrize("name", CODEC)
+def test_unsupported_formats(name):
+    for f in (q.nf4_format(0, 32, 256), q.nf4_format(0, 64, 128), q.nf4_format(2, 64, 0)):
+        assert _call(name, [_L()], f) == q.NF4_E_UNSUPPORTED
+    if name == "nf4_double_quant":
+        assert _call(name, [_L()], q.fmt(dq=False)) == q.NF4_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", CODEC)
+def test_bad_layers(name):
+    f = q.fmt()
+    assert _call(name, [], f) == q.NF4_E_ARG
+    assert _call(name, [_L(n=0)], f) == q.NF4_E_ARG
+    assert _call(name, [_L(n=-5)], f) == q.NF4_E_ARG
+    assert _call(name, [_L(n=1 << 40)], f) == q.NF4_E_ARG
+    assert _call(name, [_L(), _L(n=0)], f) == q.NF4_E_ARG
+    need = {"nf4_quantize": ["w", "codes", "absmax", "qabsmax", "scale2"],
+            "nf4_double_quant": ["absmax", "qabsmax", "scale2"],
+            "nf4_dequantize": ["codes", "qabsmax", "scale2", "out"],
+            "nf4_layer_error": ["w", "codes", "qabsmax", "scale2"]}[name]
+    for field in need:
+        assert _call(name, [_L(**{field: None})], f) == q.NF4_E_ARG, field
+    if name == "nf4_layer_error":
+        L = q.lib()
+        arr = (q.nf4_layer * 1)(_L())
+        assert L.nf4_layer_error(arr, 1, f, None, FAKE, 1 << 20, None) == q.NF4_E_ARG
+        assert L.nf4_layer_error(arr, 1, f, FAKE + 4, FAKE, 1 << 20, None) == q.NF4_E_ALIGN
+        # absmax optional with double quant, required without
+        assert _call(name, [_L(absmax=None)], q.fmt(dq=False)) == q.NF4_E_ARG
+    if name == "nf4_dequantize":
+        assert _call(name, [_L(absmax=None)], q.fmt(dq=False)) == q.NF4_E_ARG
+
+
+@pytest.mark.parametrize("name", CODEC)
+def test_misaligned_pointers(name):
+    f = q.fmt()
+    fields = {"nf4_quantize": {"w": 16, "codes": 4, "absmax": 4, "scale2": 4},
+              "nf4_double_quant": {"absmax": 4, "scale2": 4},
+              "nf4_dequantize": {"codes": 4, "scale2": 4, "out": 16},
+              "nf4_layer_error": {"w": 16, "codes": 4, "absmax": 4, "scale2": 4}}[name]
+    for field, a in fields.items():
+        for off in (1, 2, a // 2) if a > 2 else (1,):
+            if off % a:
+                assert _call(name, [_L(**{field: FAKE + off})], f) == q.NF4_E_ALIGN, (field, off)
+
+
+@pytest.mark.parametrize("name", CODEC)
+def test_workspace_checks(name):
+    f = q.fmt()
+    ns = [16384 * 5 + 3]
+    need = q.nf4_workspace_bytes(ns, f)
+    tab_only = 256
+    small = (tab_only - 1) if name != "nf4_layer_error" else (need - 1)
+    assert _call(name, [_L(n=ns[0])], f, ws=None) == q.NF4_E_WORKSPACE
+    assert _call(name, [_L(n=ns[0])], f, ws=FAKE + 64) == q.NF4_E_WORKSPACE
+    assert _call(name, [_L(n=ns[0])], f, ws_bytes=small) == q.NF4_E_WORKSPACE
+
+
+def test_select_argument_errors():
+    L = q.lib()
+    ok = dict(err=FAKE, cost=FAKE, nl=10, budget=-1, kcap=-1, sel=FAKE, k=FAKE, ws=FAKE,
+              wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.aqlora_select_topk(a["err"], a["cost"], a["nl"], a["budget"], a["kcap"],
+                                    a["sel"], a["k"], a["ws"], a["wsb"], None)
+    for fld in ("err", "cost", "sel", "k"):
+        assert call(**{fld: None}) == q.NF4_E_ARG
+    assert call(nl=0) == q.NF4_E_ARG
+    assert call(nl=65537) == q.NF4_E_ARG
+    assert call(err=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(cost=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(k=FAKE + 2) == q.NF4_E_ALIGN
+    assert call(ws=None) == q.NF4_E_WORKSPACE
+    assert call(wsb=q.aqlora_workspace_bytes(10) - 1) == q.NF4_E_WORKSPACE
+
+
+def test_status_strings():
+    for s in range(6):
+        assert q.lib().nf4_status_str(s)
+    assert q.lib().nf4_status_str(99) == b"unknown status"
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="only meaningful where no GPU exists")
+def test_hip_failure_surfaces_as_status():
+    """Valid arguments with no device: the first HIP call fails and the call
+    reports NF4_E_HIP with the HIP code kept for nf4_last_hip_error()."""
+    st = _call("nf4_quantize", [_L()], q.fmt())
+    assert st == q.NF4_E_HIP
+    assert q.lib().nf4_last_hip_error() != 0
