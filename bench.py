@@ -1,0 +1,260 @@
+"""Benchmark: GB/s of 16-bit weights through the NF4 codec and the AQLoRA pass.
+
+One step over the 14B-shaped synthetic stack (40 blocks x 7 matrices, d=5120,
+ffn=13824, bf16 N(0,0.02) with 0.05% x10 outliers, 12.69 G weights):
+  1. nf4_layer_error   -- fused absmax / NF4 encode / int8 double quant /
+                          in-register dequant / squared error, all 280 matrices
+  2. aqlora_select_topk -- rank by error, promote the top-K under 0.2 GiB
+  3. nf4_dequantize x2  -- every matrix left in NF4 back to bf16, twice (one
+                          training step's forward + backward dequant traffic)
+value = 16-bit weight bytes through the codec per second: the fused pass reads
+2 bytes per weight, each dequant pass writes 2 bytes per unpromoted weight.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s of bf16 weights through NF4 quant+dequant+error; % of HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_weight(dq: bool) -> float:
+    """Bytes each kernel must move per weight: 16-bit weight once, half a byte
+    of code, and the constants (int8 per 64 + fp32 per 16384, or fp32 per 64)."""
+    return 2.0 + 0.5 + ((1.0 / 64 + 4.0 / 16384) if dq else 4.0 / 64)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_lora_fine_nf4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_key: str, kernel: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{workload_key}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    v = vals.get(f"{kernel}_bytes_per_launch")
+    return float(v) if v else None
+
+
+def cpu_baseline(cfg, seconds: float, n_deq: int, n_total: int):
+    """The oracle (single-threaded C), untuned, on a bounded sample of the same
+    workload: slices of 64 double-quant groups from successive matrices."""
+    import numpy as np
+    import oracle
+    import synth
+    slice_n = 64 * 16384
+    done, t_fused, t_deq = 0, 0.0, 0.0
+    i = 0
+    while t_fused + t_deq < seconds:
+        w = synth.generate(cfg, i % cfg.n_layers, first=0, count=min(slice_n, cfg.n(i % cfg.n_layers)))
+        t0 = time.perf_counter()
+        r = oracle.layer_error(w, cfg.dtype, cfg.dq)
+        t1 = time.perf_counter()
+        y = oracle.dequantize(r["codes"], w.size, cfg.dtype, qabsmax=r["qabsmax"], scale2=r["scale2"])
+        t2 = time.perf_counter()
+        assert np.array_equal(y, r["y"])
+        t_fused += t1 - t0
+        t_deq += t2 - t1
+        done += w.size
+        i += 1
+    per_w_fused = t_fused / done
+    per_w_deq = t_deq / done
+    step_s = per_w_fused * n_total + cfg.dequant_repeats * per_w_deq * n_deq
+    weight_bytes = 2.0 * n_total + cfg.dequant_repeats * 2.0 * n_deq
+    return {
+        "value": weight_bytes / step_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} weights ({i} slices of 64 double-quant groups, first slice of "
+                   f"successive matrices): fused oracle pass {t_fused:.2f} s "
+                   f"({2 * done / t_fused / 1e6:.1f} MB/s of bf16), oracle dequant "
+                   f"{t_deq:.2f} s; scaled to one full step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="14b", help="toy | single | 1.4b | 7b | 14b")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_lora_fine_nf4_amd as q
+    import synth
+    from synth import configs
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        nbytes = 1 << 31
+        src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
+        return
+
+    q.lib()
+    cfg = configs.BY_NAME[args.config]
+    f = q.fmt(cfg.dtype, cfg.dq)
+    nl = cfg.n_layers
+    n_total = cfg.total
+    log(f"config {cfg.name}: {nl} matrices, {n_total} weights")
+
+    ls = q.LayerSet(cfg.sizes, f, with_absmax=not cfg.dq)
+    t0 = time.time()
+    synth.fill_device(cfg, [ls.w_of(i) for i in range(nl)],
+                      progress=lambda i: (i % 40 == 39) and log(f"generated {i + 1}/{nl} matrices"))
+    log(f"generated and uploaded in {time.time() - t0:.1f} s")
+
+    ws = torch.empty(q.nf4_workspace_bytes(ls.ns, f), dtype=torch.uint8, device="cuda")
+    err = torch.empty(nl, dtype=torch.float64, device="cuda")
+    cost = torch.tensor([q.aqlora_promote_cost(n, f) for n in cfg.sizes], dtype=torch.int64,
+                        device="cuda")
+    sel = torch.empty(nl, dtype=torch.uint8, device="cuda")
+    kout = torch.empty(1, dtype=torch.int32, device="cuda")
+    sws = torch.empty(q.aqlora_workspace_bytes(nl), dtype=torch.uint8, device="cuda")
+    budget = cfg.budgets_bytes()[0] if cfg.budgets_gib else -1
+    stream = torch.cuda.current_stream()
+    subsets = {}
+
+    def step(events=None):
+        if events is not None:
+            events["fused"][0].record(stream)
+        q.nf4_layer_error(ls, f, err, ws)
+        if events is not None:
+            events["fused"][1].record(stream)
+        q.aqlora_select_topk(err, cost, budget, cfg.kcap, sel, kout, sws)
+        keep = tuple(i for i, s in enumerate(sel.cpu().tolist()) if not s)   # synchronises
+        sub = subsets.get(keep)
+        if sub is None:
+            sub = subsets[keep] = ls.subset(keep)
+        for r in range(cfg.dequant_repeats):
+            if events is not None:
+                events["dequant"][2 * r].record(stream)
+            q.nf4_dequantize(sub, f, ws)
+            if events is not None:
+                events["dequant"][2 * r + 1].record(stream)
+        return keep
+
+    for _ in range(args.warmup):
+        keep = step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [{"fused": [torch.cuda.Event(enable_timing=True) for _ in range(2)],
+            "dequant": [torch.cuda.Event(enable_timing=True) for _ in range(2 * cfg.dequant_repeats)]}
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        keep = step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    fused_ms = sum(e["fused"][0].elapsed_time(e["fused"][1]) for e in evs) / K
+    deq_ms = [e["dequant"][2 * r].elapsed_time(e["dequant"][2 * r + 1])
+              for e in evs for r in range(cfg.dequant_repeats)]
+    deq_ms = sum(deq_ms) / max(1, len(deq_ms))
+
+    n_deq = sum(cfg.sizes[i] for i in keep)
+    bpw = algorithmic_bytes_per_weight(cfg.dq)
+    fused_bytes = bpw * n_total
+    deq_bytes = bpw * n_deq
+    weight_bytes = 2.0 * n_total + cfg.dequant_repeats * 2.0 * n_deq
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    alg_bytes = fused_bytes + cfg.dequant_repeats * deq_bytes
+    step_frac = alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    kernels = {
+        "nf4_layer_error": {"ms": round(fused_ms, 4),
+                            "algorithmic_GB": round(fused_bytes / 1e9, 4),
+                            "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1)},
+        "nf4_dequantize": {"ms": round(deq_ms, 4), "launches_per_step": cfg.dequant_repeats,
+                           "algorithmic_GB": round(deq_bytes / 1e9, 4),
+                           "GBps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1)},
+    }
+    for k in kernels.values():
+        k["frac_of_peak"] = round(k["GBps"] / HBM_PEAK_GBS, 4)
+    # dominant kernel: the larger share of the step's time
+    dom = "nf4_dequantize" if cfg.dequant_repeats * deq_ms > fused_ms else "nf4_layer_error"
+    dk = kernels[dom]
+    traffic = read_traffic(args.config, dom)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": dk["frac_of_peak"], "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "matrices": nl, "weights": n_total,
+                   "weights_dtype": "bf16" if cfg.dtype == 0 else "fp16",
+                   "double_quant": cfg.dq, "budget_bytes": budget,
+                   "promoted": nl - len(keep), "dequantized_weights": n_deq,
+                   "dequant_passes": cfg.dequant_repeats},
+        "hbm_frac_of_peak_step": round(step_frac, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, n_deq, n_total)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,9 +32,36 @@ constexpr int kLoads = kTileElems / (kThreads * 8);      // 8 x 128-bit loads pe
 constexpr int kCells = 129;                              // encode cells, trunc(64 s) in [-64, 64]
 constexpr int kRepl = 4;                                 // copies of the cell table (LDS banks)
 
+#ifndef NF4_CODEC_WAVES_PER_EU
+#define NF4_CODEC_WAVES_PER_EU 3     // at most 168 VGPRs: 3 waves per SIMD, no spills
+#endif
+#ifndef NF4_DEQUANT_WAVES_PER_EU
+#define NF4_DEQUANT_WAVES_PER_EU 4
+#endif
+#ifndef NF4_NT_STORES
+#define NF4_NT_STORES 0              // non-temporal 128-bit stores of dequantised output
+#endif
+
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 128-bit load / store unit
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// Pointers read from the layer table are generic; marking them global lets the
+// loads and stores use a scalar base plus 32-bit lane offsets.
+#define GLOBAL __attribute__((address_space(1)))
+typedef const GLOBAL uint16_t* g_cu16;
+typedef const GLOBAL u32x4* g_cu4;
+typedef const GLOBAL uint8_t* g_cu8;
+typedef const GLOBAL uint32_t* g_cu32;
+typedef const GLOBAL int8_t* g_ci8;
+typedef const GLOBAL float* g_cf32;
+typedef GLOBAL uint8_t* g_u8;
+typedef GLOBAL uint32_t* g_u32;
+typedef GLOBAL uint16_t* g_u16;
+typedef GLOBAL u32x4* g_u4;
+typedef GLOBAL int8_t* g_i8;
+typedef GLOBAL float* g_f32;
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -80,7 +107,7 @@ __device__ void build_cells(EncCell* cells)
 
 // largest |x| bit pattern of 8 packed 16-bit values (sign-magnitude formats:
 // for non-negative values the integer order is the numeric order)
-__device__ __forceinline__ uint32_t absmax_bits8(const uint4 v)
+__device__ __forceinline__ uint32_t absmax_bits8(const u32x4 v)
 {
     const uint32_t m = 0x7fff7fffu;
     us2 a = __builtin_bit_cast(us2, v.x & m), b = __builtin_bit_cast(us2, v.y & m);
@@ -116,6 +143,17 @@ __device__ __forceinline__ float opaque(float x)
 {
     __asm__ volatile("" : "+v"(x));
     return x;
+}
+
+// Element offset of this lane's first weight within a tile (wave w, lane L:
+// 4096 w + 8 L); load j adds 512 j.  Recomputed per tile behind an opaque
+// barrier: hoisted out of the tile loop, the 8 derived 64-bit addresses per
+// buffer would stay live across tiles and spill.
+__device__ __forceinline__ uint32_t lane_base()
+{
+    uint32_t b = (threadIdx.x >> 6) * 4096u + (threadIdx.x & 63u) * 8u;
+    __asm__ volatile("" : "+v"(b));
+    return b;
 }
 
 // Round two fp32 values to the 16-bit type (nearest, ties to even) and return
@@ -218,16 +256,17 @@ struct CodecShared {
 // 2^k before squaring so that the fp32 squares neither underflow nor
 // overflow (exact; undone in fp64).
 template <int DT, bool ERR, bool FULL, bool SPEC>
-__device__ __forceinline__ double encode_lane(const CodecShared& sh, const uint4 (&v)[kLoads],
-                                              uint8_t* __restrict__ cp, int valid)
+__device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4 (&v)[kLoads],
+                                              g_u8 cp, int valid)
 {
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
     const EncCell* cells = sh.cells + (lane & (kRepl - 1));
+    const uint32_t lb = lane_base();
     double acc64 = 0.0;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-        const int o = wv * 4096 + j * 512 + lane * 8;
-        const int bidx = wv * 64 + j * 8 + (lane >> 3);
+        const uint32_t o = lb + j * 512u;
+        const int bidx = (int)(o >> 6);
         const f2 bk = sh.blk[bidx];
         float scale = 1.0f;
         int ek = 0;
@@ -263,52 +302,61 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const uint4
                 e = __builtin_fmaf(d1, d1, e);
             }
             if constexpr (!FULL) {
-                if (o + 2 * k2 >= valid) code0 = 0;
-                if (o + 2 * k2 + 1 >= valid) code1 = 0;
+                if (o + 2 * k2 >= (uint32_t)valid) code0 = 0;
+                if (o + 2 * k2 + 1 >= (uint32_t)valid) code1 = 0;
             }
             pk |= (code0 << (8 * k2)) | (code1 << (8 * k2 + 4));
         }
         if constexpr (FULL) {
-            *(uint32_t*)(cp + (o >> 1)) = pk;
+            *(g_u32)(cp + (o >> 1)) = pk;
         } else {
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
-                if (o + 2 * bb < valid) cp[(o >> 1) + bb] = (uint8_t)(pk >> (8 * bb));
+                if (o + 2 * bb < (uint32_t)valid) cp[(o >> 1) + bb] = (uint8_t)(pk >> (8 * bb));
         }
         if constexpr (ERR) {
             const double blk_sse = (double)sum8_f32(e);
             acc64 += SPEC ? __builtin_ldexp(blk_sse, -2 * ek) : blk_sse;
         }
+        // keep the scheduler from hoisting the next group's lookups (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
     }
     return acc64;
 }
 
-template <int DT, bool DQ, bool ERR, bool FULL>
-__device__ __forceinline__ void codec_tile(CodecShared& sh, const TileRef& tr, int64_t tile,
-                                           double* __restrict__ partial)
+// 1. the tile's weights into registers: 8 x 128-bit loads per lane (a ragged
+// last tile loads element by element and pads with zeros)
+__device__ __forceinline__ void load_tile(u32x4 (&v)[kLoads], const TileRef& tr)
 {
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const LayerDesc& d = *tr.d;
-    const uint16_t* __restrict__ w = (const uint16_t*)d.w + tr.e0;
+    const g_cu16 w = (g_cu16)tr.d->w + tr.e0;
     const int valid = tr.valid;
-
-    // 1. 128-bit loads, 8 per lane (the whole tile in registers)
-    uint4 v[kLoads];
+    const uint32_t lb = lane_base();
+    if (valid == kTileElems) {
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const int o = wv * 4096 + j * 512 + lane * 8;
-        if constexpr (FULL) {
-            v[j] = *(const uint4*)(w + o);
-        } else {
+        for (int j = 0; j < kLoads; ++j) v[j] = *(g_cu4)(w + (lb + j * 512u));
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const uint32_t o = lb + j * 512u;
             uint16_t h[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) h[k] = (o + k < valid) ? w[o + k] : (uint16_t)0;
+            for (int k = 0; k < 8; ++k) h[k] = (o + k < (uint32_t)valid) ? w[o + k] : (uint16_t)0;
             v[j].x = h[0] | ((uint32_t)h[1] << 16);
             v[j].y = h[2] | ((uint32_t)h[3] << 16);
             v[j].z = h[4] | ((uint32_t)h[5] << 16);
             v[j].w = h[6] | ((uint32_t)h[7] << 16);
         }
     }
+}
+
+template <int DT, bool DQ, bool ERR>
+__device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[kLoads],
+                                              const TileRef& tr, int64_t tile,
+                                              double* __restrict__ partial)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const LayerDesc& d = *tr.d;
+    const int valid = tr.valid;
 
     // 2. block absmax (exact: a max of representable values)
 #pragma unroll
@@ -360,19 +408,24 @@ __device__ __forceinline__ void codec_tile(CodecShared& sh, const TileRef& tr, i
         const int nbv = (valid + 63) >> 6;
         const int64_t b = (tr.e0 >> 6) + t;
         if (t < nbv) {
-            if (d.absmax) d.absmax[b] = a;
-            if constexpr (DQ) d.qabsmax[b] = q;
+            if (d.absmax) ((g_f32)d.absmax)[b] = a;
+            if constexpr (DQ) ((g_i8)d.qabsmax)[b] = q;
         }
         if constexpr (DQ) {
-            if (t == 0) d.scale2[tr.local] = s2;
+            if (t == 0) ((g_f32)d.scale2)[tr.local] = s2;
         }
     }
     const int any_spec = __syncthreads_or(pre != 1.0f || ek != 0);
 
     // 4. encode, pack, store codes; dequantise in registers and square the error
-    uint8_t* __restrict__ cp = d.codes + (tr.e0 >> 1);
-    const double acc = any_spec ? encode_lane<DT, ERR, FULL, true>(sh, v, cp, valid)
-                                : encode_lane<DT, ERR, FULL, false>(sh, v, cp, valid);
+    const g_u8 cp = (g_u8)d.codes + (tr.e0 >> 1);
+    double acc;
+    if (valid == kTileElems)
+        acc = any_spec ? encode_lane<DT, ERR, true, true>(sh, v, cp, valid)
+                       : encode_lane<DT, ERR, true, false>(sh, v, cp, valid);
+    else
+        acc = any_spec ? encode_lane<DT, ERR, false, true>(sh, v, cp, valid)
+                       : encode_lane<DT, ERR, false, false>(sh, v, cp, valid);
 
     if constexpr (ERR) {
         // lanes of one block group hold the same sum; add the 8 groups in a fixed tree
@@ -386,91 +439,148 @@ __device__ __forceinline__ void codec_tile(CodecShared& sh, const TileRef& tr, i
     }
 }
 
+// Persistent grid-stride walk over the flat tile index, software-pipelined:
+// the next tile's loads are issued before the current tile is processed
+// (unrolled by two so the register buffers swap roles without copies).
 template <int DT, bool DQ, bool ERR>
-__global__ __launch_bounds__(kThreads) void k_codec(const LayerDesc* __restrict__ tab, int nl,
-                                                    int64_t ntiles, double* __restrict__ partial)
+__global__ __launch_bounds__(kThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
+    const LayerDesc* __restrict__ tab, int nl, int64_t ntiles, double* __restrict__ partial)
 {
     __shared__ CodecShared sh;
     build_cells(sh.cells);
     __syncthreads();
     if ((int64_t)blockIdx.x >= ntiles) return;
     int l = first_layer(tab, nl, blockIdx.x);
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const TileRef tr = tile_ref(tab, l, tile);
-        if (tr.valid == kTileElems) codec_tile<DT, DQ, ERR, true>(sh, tr, tile, partial);
-        else                        codec_tile<DT, DQ, ERR, false>(sh, tr, tile, partial);
+    int64_t tile = blockIdx.x;
+    TileRef tr0 = tile_ref(tab, l, tile), tr1;
+    u32x4 v0[kLoads], v1[kLoads];
+    load_tile(v0, tr0);
+    for (;;) {
+        int64_t nxt = tile + gridDim.x;
+        bool more = nxt < ntiles;
+        if (more) { tr1 = tile_ref(tab, l, nxt); load_tile(v1, tr1); }
+        codec_compute<DT, DQ, ERR>(sh, v0, tr0, tile, partial);
+        if (!more) break;
+        tile = nxt;
+        nxt = tile + gridDim.x;
+        more = nxt < ntiles;
+        if (more) { tr0 = tile_ref(tab, l, nxt); load_tile(v0, tr0); }
+        codec_compute<DT, DQ, ERR>(sh, v1, tr1, tile, partial);
+        if (!more) break;
+        tile = nxt;
     }
 }
 
 // ---- standalone dequantisation -------------------------------------------
 
-template <int DT, bool DQ, bool FULL>
-__device__ __forceinline__ void dequant_tile(const float* s_lv, const TileRef& tr)
+// Codes and constants of one tile for one lane: 8 dwords of packed codes
+// (8 weights each) and the raw constant of each dword's block.
+struct DqIn {
+    uint32_t c32[kLoads];
+    float own;   // constant of block 64 w + L: int8 qabsmax as float, or the fp32 absmax
+};
+
+template <bool DQ>
+__device__ __forceinline__ void load_dq(DqIn& r, const TileRef& tr)
 {
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const LayerDesc& d = *tr.d;
     const int valid = tr.valid;
-    const uint8_t* __restrict__ cp = d.codes + (tr.e0 >> 1);
-    uint16_t* __restrict__ outp = (uint16_t*)d.out + tr.e0;
-    const int64_t b0 = tr.e0 >> 6;
-    const float s2 = DQ ? d.scale2[tr.local] : 0.0f;
-
-    uint32_t c32[kLoads];
-    float adq[kLoads];
+    const g_cu8 cp = (g_cu8)d.codes + (tr.e0 >> 1);
+    const uint32_t lb = lane_base();
+    if (valid == kTileElems) {
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const int o = wv * 4096 + j * 512 + lane * 8;
-        const int64_t b = b0 + (o >> 6);
-        if constexpr (FULL) {
-            c32[j] = *(const uint32_t*)(cp + (o >> 1));
-        } else {
+        for (int j = 0; j < kLoads; ++j) r.c32[j] = *(g_cu32)(cp + ((lb + j * 512u) >> 1));
+    } else {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const uint32_t o = lb + j * 512u;
             uint32_t c = 0;
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
-                if (o + 2 * bb < valid) c |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
-            c32[j] = c;
-        }
-        if (FULL || o < valid) {
-            if constexpr (DQ) adq[j] = (float)d.qabsmax[b] * s2;
-            else              adq[j] = d.absmax[b];
-        } else {
-            adq[j] = 0.0f;
+                if (o + 2 * bb < (uint32_t)valid) c |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
+            r.c32[j] = c;
         }
     }
+    // the lane's own block within the tile: wave w, lane L -> block 64 w + L
+    const uint32_t blk = threadIdx.x;
+    const bool in = (blk << 6) < (uint32_t)valid;
+    if constexpr (DQ) r.own = in ? (float)((g_ci8)d.qabsmax + (tr.e0 >> 6))[blk] : 0.0f;
+    else              r.own = in ? ((g_cf32)d.absmax + (tr.e0 >> 6))[blk] : 0.0f;
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(GLOBAL T* p, const T& v)
+{
+#if NF4_NT_STORES
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+template <int DT, bool DQ>
+__device__ __forceinline__ void dequant_compute(const float* s_lv, const DqIn& r, const TileRef& tr)
+{
+    const int lane = threadIdx.x & 63;
+    const LayerDesc& d = *tr.d;
+    const int valid = tr.valid;
+    const g_u16 outp = (g_u16)d.out + tr.e0;
+    const float s2 = DQ ? ((g_cf32)d.scale2)[tr.local] : 1.0f;
+    const bool full = valid == kTileElems;
+    const uint32_t lb = lane_base();
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-        const int o = wv * 4096 + j * 512 + lane * 8;
+        const uint32_t o = lb + j * 512u;
+        // block of this dword: 64 w + 8 j + L/8 -> held by lane 8 j + L/8 of the wave
+        const float kj = __builtin_bit_cast(float, __shfl(__builtin_bit_cast(int, r.own),
+                                                          8 * j + (lane >> 3), 64));
+        const float adq = DQ ? kj * s2 : kj;
         uint32_t p[4];
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {
-            const float y0 = s_lv[(c32[j] >> (8 * k2)) & 15] * adq[j];
-            const float y1 = s_lv[(c32[j] >> (8 * k2 + 4)) & 15] * adq[j];
+            const float y0 = s_lv[(r.c32[j] >> (8 * k2)) & 15] * adq;
+            const float y1 = s_lv[(r.c32[j] >> (8 * k2 + 4)) & 15] * adq;
             float r0, r1;
             p[k2] = round_pair<DT>(y0, y1, r0, r1);
         }
-        if constexpr (FULL) {
-            *(uint4*)(outp + o) = uint4{p[0], p[1], p[2], p[3]};
+        if (full) {
+            u32x4 pv = {p[0], p[1], p[2], p[3]};
+            store16((g_u4)(outp + o), pv);
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                if (o + k < valid) outp[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
+                if (o + k < (uint32_t)valid) outp[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 template <int DT, bool DQ>
-__global__ __launch_bounds__(kThreads) void k_dequant(const LayerDesc* __restrict__ tab, int nl,
-                                                      int64_t ntiles)
+__global__ __launch_bounds__(kThreads, NF4_DEQUANT_WAVES_PER_EU) void k_dequant(
+    const LayerDesc* __restrict__ tab, int nl, int64_t ntiles)
 {
     __shared__ float s_lv[16];
     if (threadIdx.x < 16) s_lv[threadIdx.x] = as_f(nf4fmt::kLevelBits[threadIdx.x]);
     __syncthreads();
     if ((int64_t)blockIdx.x >= ntiles) return;
     int l = first_layer(tab, nl, blockIdx.x);
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const TileRef tr = tile_ref(tab, l, tile);
-        if (tr.valid == kTileElems) dequant_tile<DT, DQ, true>(s_lv, tr);
-        else                        dequant_tile<DT, DQ, false>(s_lv, tr);
+    int64_t tile = blockIdx.x;
+    TileRef tr0 = tile_ref(tab, l, tile), tr1;
+    DqIn r0, r1;
+    load_dq<DQ>(r0, tr0);
+    for (;;) {
+        int64_t nxt = tile + gridDim.x;
+        bool more = nxt < ntiles;
+        if (more) { tr1 = tile_ref(tab, l, nxt); load_dq<DQ>(r1, tr1); }
+        dequant_compute<DT, DQ>(s_lv, r0, tr0);
+        if (!more) break;
+        tile = nxt;
+        nxt = tile + gridDim.x;
+        more = nxt < ntiles;
+        if (more) { tr0 = tile_ref(tab, l, nxt); load_dq<DQ>(r0, tr0); }
+        dequant_compute<DT, DQ>(s_lv, r1, tr1);
+        if (!more) break;
+        tile = nxt;
     }
 }
 
@@ -488,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void k_double_quant(const LayerDesc* __re
         const LayerDesc& d = *tr.d;
         const int nbv = (tr.valid + 63) >> 6;
         const int64_t b = (tr.e0 >> 6) + t;
-        const float a = (t < nbv) ? d.absmax[b] : 0.0f;
+        const float a = (t < nbv) ? ((g_cf32)d.absmax)[b] : 0.0f;
         const uint32_t wm = wave_max_u32(as_u(a));
         if (lane == 0) s_wmax[wv] = wm;
         __syncthreads();
@@ -504,8 +614,8 @@ __global__ __launch_bounds__(kThreads) void k_double_quant(const LayerDesc* __re
             qf = fminf(fmaxf(qf, -127.0f), 127.0f);
             q = (int8_t)qf;
         }
-        if (t < nbv) d.qabsmax[b] = q;
-        if (t == 0) d.scale2[tr.local] = s2;
+        if (t < nbv) ((g_i8)d.qabsmax)[b] = q;
+        if (t == 0) ((g_f32)d.scale2)[tr.local] = s2;
     }
 }
 
