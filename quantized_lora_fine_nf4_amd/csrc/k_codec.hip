@@ -27,16 +27,24 @@
 namespace nf4k {
 namespace {
 
-constexpr int kWaves = kThreads / 64;                    // 4
+constexpr int kWaves = kThreads / 64;                    // 4 waves, each owning 64 blocks of a tile
 constexpr int kLoads = kTileElems / (kThreads * 8);      // 8 x 128-bit loads per lane
+constexpr int kCThreads = kThreads;                      // fused kernel workgroup
+constexpr int kCWaves = kWaves;
+constexpr int kCLoads = kLoads;
+static_assert(kPartsPerTile == kCWaves, "one fp64 error partial per wave and tile");
 constexpr int kCells = 129;                              // encode cells, trunc(64 s) in [-64, 64]
-constexpr int kRepl = 4;                                 // copies of the cell table (LDS banks)
+constexpr int kRepl = 16;    // lane-indexed copies of the cell table: conflict-free 64-bit reads
+constexpr int kYStride = 256 + 17;   // per-block dequant table, code-major, odd pad against bank conflicts
 
 #ifndef NF4_CODEC_WAVES_PER_EU
 #define NF4_CODEC_WAVES_PER_EU 3     // at most 168 VGPRs: 3 waves per SIMD, no spills
 #endif
 #ifndef NF4_DEQUANT_WAVES_PER_EU
 #define NF4_DEQUANT_WAVES_PER_EU 4
+#endif
+#ifndef NF4_SCHED_FENCE
+#define NF4_SCHED_FENCE 1            // scheduling fence every 8 (1) or 4 (2) weights in the fused kernel
 #endif
 #ifndef NF4_NT_STORES
 #define NF4_NT_STORES 0              // non-temporal 128-bit stores of dequantised output
@@ -74,16 +82,14 @@ __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(ui
 //   base = number of thresholds strictly below the cell.
 // u and thr are exact scalings by 64 of s and the fp32 threshold, so the
 // comparison is exactly "threshold < s".
-struct alignas(16) EncCell {
+struct alignas(8) EncCell {
     float thr;
     uint32_t base;
-    float lv_lo;   // level[base]
-    float lv_hi;   // level[base + 1] (unused when thr is +inf)
 };
 
 __device__ void build_cells(EncCell* cells)
 {
-    for (int idx = threadIdx.x; idx < kCells * kRepl; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < kCells * kRepl; idx += kCThreads) {
         const int k = idx / kRepl - 64;
         const float lo = (k > 0) ? (float)k : (k < 0 ? (float)(k - 1) : -1.0f);
         const float hi = (k > 0) ? (float)(k + 1) : (k < 0 ? (float)k : 1.0f);
@@ -94,12 +100,7 @@ __device__ void build_cells(EncCell* cells)
             if (t64 < lo) ++base;
             else if (t64 <= hi) thr = t64;
         }
-        EncCell c;
-        c.thr = thr;
-        c.base = base;
-        c.lv_lo = as_f(nf4fmt::kLevelBits[base]);
-        c.lv_hi = as_f(nf4fmt::kLevelBits[base < 15 ? base + 1 : 15]);
-        cells[idx] = c;
+        cells[idx] = EncCell{thr, base};
     }
 }
 
@@ -145,13 +146,14 @@ __device__ __forceinline__ float opaque(float x)
     return x;
 }
 
-// Element offset of this lane's first weight within a tile (wave w, lane L:
-// 4096 w + 8 L); load j adds 512 j.  Recomputed per tile behind an opaque
+// Element offset of this lane's first weight within a tile (wave w of W,
+// lane L: (16384 / W) w + 8 L); load j adds 512 j.  Recomputed per tile behind an opaque
 // barrier: hoisted out of the tile loop, the 8 derived 64-bit addresses per
 // buffer would stay live across tiles and spill.
+template <int THREADS = kThreads>
 __device__ __forceinline__ uint32_t lane_base()
 {
-    uint32_t b = (threadIdx.x >> 6) * 4096u + (threadIdx.x & 63u) * 8u;
+    uint32_t b = (threadIdx.x >> 6) * (uint32_t)(kTileElems / (THREADS / 64)) + (threadIdx.x & 63u) * 8u;
     __asm__ volatile("" : "+v"(b));
     return b;
 }
@@ -197,10 +199,47 @@ __device__ __forceinline__ float sum8_f32(float v)
     return v;
 }
 
+// fp64 sum over the 64 lanes of a wave, fixed order: within each row of 16
+// lanes by DPP (xor 1, xor 2, half-row mirror, row mirror; every lane of a
+// row ends with the same value), then the four row sums in order.  Valid in
+// every lane.
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    v += dpp_mov_f64<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov_f64<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov_f64<0x141>(v);   // row_half_mirror
+    v += dpp_mov_f64<0x140>(v);   // row_mirror
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    double r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 16 * i);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 16 * i);
+        r[i] = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    }
+    return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    return v;
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
 }
 
 // ---- tile walk ---------------------------------------------------------
@@ -237,37 +276,45 @@ __device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_
 
 // ---- fused quantise / double-quantise / dequantise / error --------------
 
+// LDS of the fused kernel.  Everything per block is private to the wave that
+// owns the block (wave w: blocks 64 w .. 64 w + 63 of the tile), so a wave
+// reads back only what it wrote itself; the one cross-wave value is each
+// wave's largest absmax for the double-quant group maximum, double-buffered by
+// tile parity so that a wave one tile ahead never overwrites a value another
+// wave still reads.
 struct CodecShared {
     EncCell cells[kCells * kRepl];
-    uint32_t amax[256];      // block absmax bits (16-bit pattern)
-    f2 blk[256];             // per block: (64 / absmax [scaled], dequantised absmax)
-    float pre[256];          // per block: 2^64 when absmax < 2^-100, else 1
-    int escale[256];         // per block: k with absmax * 2^k in [1, 2) for extreme absmax, else 0
-    uint32_t wmax[kWaves];
-    double wsum[kWaves];
+    float ytab[16 * kYStride];  // ytab[c * kYStride + b] = RNE16(level[c] * dequantised absmax of block b)
+    uint32_t amax[256];         // block absmax bits (16-bit pattern)
+    float r64[256];             // per block: 64 / absmax (of the 2^64-scaled absmax when tiny)
+    float pre[256];             // per block: 2^64 when absmax < 2^-100, else 1
+    int escale[256];            // per block: k with absmax * 2^k in [1, 2) for extreme absmax, else 0
+    uint32_t wmax[2][kCWaves];  // per tile parity, per wave: largest absmax bits of the wave's blocks
 };
 
 // Step 4 of a tile for one lane: encode, pack and store the codes of its 64
-// weights; with ERR also dequantise them in registers and add up the squared
-// differences (fp32 over the 64 weights of a block, fp64 across blocks).
+// weights; with ERR also look up each weight's dequantised value in the
+// block's table and add up the squared differences in fp32 over the lane's 64
+// weights (the caller adds the lanes in fp64).
 // SPEC is the rare wave-uniform path for blocks with extreme absmax: the
 // weights are scaled by 2^64 before normalising (absmax < 2^-100, keeps 64/a
 // finite and leaves the codes unchanged), and each difference is scaled by
 // 2^k before squaring so that the fp32 squares neither underflow nor
-// overflow (exact; undone in fp64).
+// overflow (exact; undone in fp64 per block, counted once per 8-lane group).
 template <int DT, bool ERR, bool FULL, bool SPEC>
-__device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4 (&v)[kLoads],
+__device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4 (&v)[kCLoads],
                                               g_u8 cp, int valid)
 {
-    const int t = threadIdx.x, lane = t & 63;
+    const int lane = threadIdx.x & 63;
     const EncCell* cells = sh.cells + (lane & (kRepl - 1));
-    const uint32_t lb = lane_base();
+    const uint32_t lb = lane_base<kCThreads>();
+    float e = 0.0f;
     double acc64 = 0.0;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kCLoads; ++j) {
         const uint32_t o = lb + j * 512u;
         const int bidx = (int)(o >> 6);
-        const f2 bk = sh.blk[bidx];
+        const float r64 = sh.r64[bidx];
         float scale = 1.0f;
         int ek = 0;
         if constexpr (SPEC) {
@@ -276,36 +323,33 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
         }
         const uint32_t dw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t pk = 0;
-        float e = 0.0f;
+        float eb = 0.0f;
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {
-            float x0, x1;
-            unpack2<DT>(dw[k2], x0, x1);
-            const float u0 = (SPEC ? x0 * scale : x0) * bk.x;
-            const float u1 = (SPEC ? x1 * scale : x1) * bk.x;
-            const EncCell c0 = cells[((int)u0 + 64) * kRepl];
-            const EncCell c1 = cells[((int)u1 + 64) * kRepl];
-            const bool h0 = u0 > c0.thr, h1 = u1 > c1.thr;
-            uint32_t code0 = c0.base + (h0 ? 1u : 0u);
-            uint32_t code1 = c1.base + (h1 ? 1u : 0u);
-            if constexpr (ERR) {
-                const float y0 = (h0 ? c0.lv_hi : c0.lv_lo) * bk.y;
-                const float y1 = (h1 ? c1.lv_hi : c1.lv_lo) * bk.y;
-                float r0, r1;
-                (void)round_pair<DT>(y0, y1, r0, r1);
-                float d0 = x0 - r0, d1 = x1 - r1;
-                if constexpr (SPEC) {
-                    d0 = __builtin_amdgcn_ldexpf(d0, ek);
-                    d1 = __builtin_amdgcn_ldexpf(d1, ek);
+#if NF4_SCHED_FENCE == 2
+            if (k2 == 2) __builtin_amdgcn_sched_barrier(0);
+#endif
+            float x[2];
+            unpack2<DT>(dw[k2], x[0], x[1]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float u = (SPEC ? x[h] * scale : x[h]) * r64;
+                const EncCell c = cells[((int)u + 64) * kRepl];
+                uint32_t code = c.base + (u > c.thr ? 1u : 0u);
+                if constexpr (ERR) {
+                    float dd = x[h] - sh.ytab[__umul24(code, (uint32_t)kYStride) + (uint32_t)bidx];
+                    if constexpr (SPEC) {
+                        dd = __builtin_amdgcn_ldexpf(dd, ek);
+                        eb = __builtin_fmaf(dd, dd, eb);
+                    } else {
+                        e = __builtin_fmaf(dd, dd, e);
+                    }
                 }
-                e = __builtin_fmaf(d0, d0, e);
-                e = __builtin_fmaf(d1, d1, e);
+                if constexpr (!FULL) {
+                    if (o + 2 * k2 + h >= (uint32_t)valid) code = 0;
+                }
+                pk |= code << (8 * k2 + 4 * h);
             }
-            if constexpr (!FULL) {
-                if (o + 2 * k2 >= (uint32_t)valid) code0 = 0;
-                if (o + 2 * k2 + 1 >= (uint32_t)valid) code1 = 0;
-            }
-            pk |= (code0 << (8 * k2)) | (code1 << (8 * k2 + 4));
         }
         if constexpr (FULL) {
             *(g_u32)(cp + (o >> 1)) = pk;
@@ -314,29 +358,30 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
             for (int bb = 0; bb < 4; ++bb)
                 if (o + 2 * bb < (uint32_t)valid) cp[(o >> 1) + bb] = (uint8_t)(pk >> (8 * bb));
         }
-        if constexpr (ERR) {
-            const double blk_sse = (double)sum8_f32(e);
-            acc64 += SPEC ? __builtin_ldexp(blk_sse, -2 * ek) : blk_sse;
+        if constexpr (ERR && SPEC) {
+            const double blk_sse = __builtin_ldexp((double)sum8_f32(eb), -2 * ek);
+            if ((lane & 7) == 0) acc64 += blk_sse;
         }
         // keep the scheduler from hoisting the next group's lookups (register pressure)
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (ERR && !SPEC) acc64 = (double)e;
     return acc64;
 }
 
 // 1. the tile's weights into registers: 8 x 128-bit loads per lane (a ragged
 // last tile loads element by element and pads with zeros)
-__device__ __forceinline__ void load_tile(u32x4 (&v)[kLoads], const TileRef& tr)
+__device__ __forceinline__ void load_tile(u32x4 (&v)[kCLoads], const TileRef& tr)
 {
     const g_cu16 w = (g_cu16)tr.d->w + tr.e0;
     const int valid = tr.valid;
-    const uint32_t lb = lane_base();
+    const uint32_t lb = lane_base<kCThreads>();
     if (valid == kTileElems) {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) v[j] = *(g_cu4)(w + (lb + j * 512u));
+        for (int j = 0; j < kCLoads; ++j) v[j] = *(g_cu4)(w + (lb + j * 512u));
     } else {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
+        for (int j = 0; j < kCLoads; ++j) {
             const uint32_t o = lb + j * 512u;
             uint16_t h[8];
 #pragma unroll
@@ -350,35 +395,40 @@ __device__ __forceinline__ void load_tile(u32x4 (&v)[kLoads], const TileRef& tr)
 }
 
 template <int DT, bool DQ, bool ERR>
-__device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[kLoads],
-                                              const TileRef& tr, int64_t tile,
+__device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[kCLoads],
+                                              const TileRef& tr, int64_t tile, int parity,
                                               double* __restrict__ partial)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const LayerDesc& d = *tr.d;
     const int valid = tr.valid;
 
-    // 2. block absmax (exact: a max of representable values)
+    // 2. block absmax (exact: a max of representable values), and the wave's
+    //    largest for the double-quant group maximum
+    const uint32_t lb = lane_base<kCThreads>();
+    uint32_t wm = 0;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kCLoads; ++j) {
         const uint32_t m = max8_u32(absmax_bits8(v[j]));
-        if ((lane & 7) == 0) sh.amax[wv * 64 + j * 8 + (lane >> 3)] = m;
+        if ((lane & 7) == 0) sh.amax[(lb + j * 512u) >> 6] = m;
+        wm = max(wm, m);
     }
-    __syncthreads();
+    if constexpr (DQ) {
+        wm = wave_max_u32(wm);
+        if (lane == 0) sh.wmax[parity][wv] = wm;
+        __syncthreads();   // the only workgroup barrier of a tile
+    }
 
-    // 3. per-block constants, thread t owns block t of the tile
+    // 3. constants of the wave's 64 blocks: lane L owns block b = 64 w + L = t
     const float a = f16bits_to_f32<DT>(sh.amax[t]);
     float adq = a;
     int8_t q = 0;
     float s2 = 0.0f;
     if constexpr (DQ) {
-        const uint32_t wm = wave_max_u32(as_u(a));
-        if (lane == 0) sh.wmax[wv] = wm;
-        __syncthreads();
-        uint32_t g = sh.wmax[0];
+        uint32_t g = sh.wmax[parity][0];
 #pragma unroll
-        for (int i = 1; i < kWaves; ++i) g = max(g, sh.wmax[i]);
-        const float G = as_f(g);
+        for (int i = 1; i < kCWaves; ++i) g = max(g, sh.wmax[parity][i]);
+        const float G = f16bits_to_f32<DT>(g);
         if (G > 0.0f) {
             s2 = G / 127.0f;
             float qf = rintf(a / s2);
@@ -401,9 +451,20 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
         }
         if (ERR && (a < 0x1p-40f || a >= 0x1p40f)) ek = 1 - __builtin_amdgcn_frexp_expf(a);
     }
-    sh.blk[t] = f2{r64, adq};
+    sh.r64[t] = r64;
     sh.pre[t] = pre;
     sh.escale[t] = ek;
+    if constexpr (ERR) {
+        // the block's 16 dequantised values, rounded to the 16-bit type, back in fp32
+#pragma unroll
+        for (int c = 0; c < 16; c += 2) {
+            float y0, y1;
+            (void)round_pair<DT>(as_f(nf4fmt::kLevelBits[c]) * adq,
+                                 as_f(nf4fmt::kLevelBits[c + 1]) * adq, y0, y1);
+            sh.ytab[c * kYStride + t] = y0;
+            sh.ytab[(c + 1) * kYStride + t] = y1;
+        }
+    }
     {
         const int nbv = (valid + 63) >> 6;
         const int64_t b = (tr.e0 >> 6) + t;
@@ -415,9 +476,11 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
             if (t == 0) ((g_f32)d.scale2)[tr.local] = s2;
         }
     }
-    const int any_spec = __syncthreads_or(pre != 1.0f || ek != 0);
+    // the wave reads back only its own blocks' constants: LDS keeps a wave's
+    // accesses in order, no barrier needed
+    const bool any_spec = __builtin_amdgcn_ballot_w64(pre != 1.0f || ek != 0) != 0;
 
-    // 4. encode, pack, store codes; dequantise in registers and square the error
+    // 4. encode, pack, store codes; look up the dequantised values and square the error
     const g_u8 cp = (g_u8)d.codes + (tr.e0 >> 1);
     double acc;
     if (valid == kTileElems)
@@ -427,15 +490,11 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
         acc = any_spec ? encode_lane<DT, ERR, false, true>(sh, v, cp, valid)
                        : encode_lane<DT, ERR, false, false>(sh, v, cp, valid);
 
+    // 5. the wave's fp64 partial (64 lanes in a fixed order); tiles and waves
+    //    are added per layer by k_reduce
     if constexpr (ERR) {
-        // lanes of one block group hold the same sum; add the 8 groups in a fixed tree
-        double acc64 = acc;
-        acc64 += __shfl_xor(acc64, 8, 64);
-        acc64 += __shfl_xor(acc64, 16, 64);
-        acc64 += __shfl_xor(acc64, 32, 64);
-        if (lane == 0) sh.wsum[wv] = acc64;
-        __syncthreads();
-        if (t == 0) partial[tile] = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
+        const double acc64 = wave_sum_f64(acc);
+        if (lane == 0) partial[tile * kPartsPerTile + wv] = acc64;
     }
 }
 
@@ -443,7 +502,7 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 // the next tile's loads are issued before the current tile is processed
 // (unrolled by two so the register buffers swap roles without copies).
 template <int DT, bool DQ, bool ERR>
-__global__ __launch_bounds__(kThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
+__global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
     const LayerDesc* __restrict__ tab, int nl, int64_t ntiles, double* __restrict__ partial)
 {
     __shared__ CodecShared sh;
@@ -453,19 +512,19 @@ __global__ __launch_bounds__(kThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
     int l = first_layer(tab, nl, blockIdx.x);
     int64_t tile = blockIdx.x;
     TileRef tr0 = tile_ref(tab, l, tile), tr1;
-    u32x4 v0[kLoads], v1[kLoads];
+    u32x4 v0[kCLoads], v1[kCLoads];
     load_tile(v0, tr0);
     for (;;) {
         int64_t nxt = tile + gridDim.x;
         bool more = nxt < ntiles;
         if (more) { tr1 = tile_ref(tab, l, nxt); load_tile(v1, tr1); }
-        codec_compute<DT, DQ, ERR>(sh, v0, tr0, tile, partial);
+        codec_compute<DT, DQ, ERR>(sh, v0, tr0, tile, 0, partial);
         if (!more) break;
         tile = nxt;
         nxt = tile + gridDim.x;
         more = nxt < ntiles;
         if (more) { tr0 = tile_ref(tab, l, nxt); load_tile(v0, tr0); }
-        codec_compute<DT, DQ, ERR>(sh, v1, tr1, tile, partial);
+        codec_compute<DT, DQ, ERR>(sh, v1, tr1, tile, 1, partial);
         if (!more) break;
         tile = nxt;
     }
@@ -627,8 +686,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const LayerDesc* __restrict
 {
     __shared__ double s[kThreads];
     const int l = blockIdx.x, t = threadIdx.x;
-    const int64_t end = tab[l].tile_end;
-    const int64_t begin = end - tiles_of(tab[l].n);
+    const int64_t end = tab[l].tile_end * kPartsPerTile;
+    const int64_t begin = end - tiles_of(tab[l].n) * kPartsPerTile;
     double acc = 0.0;
     for (int64_t i = begin + t; i < end; i += kThreads) acc += partial[i];
     s[t] = acc;
@@ -652,10 +711,10 @@ int cu_count()
 }
 
 template <typename K>
-int64_t persistent_grid(K kernel, int64_t ntiles)
+int64_t persistent_grid(K kernel, int64_t ntiles, int threads = kThreads)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
         per_cu <= 0)
         per_cu = 4;
     const int64_t g = (int64_t)cu_count() * per_cu;
@@ -666,8 +725,8 @@ template <int DT, bool DQ, bool ERR>
 hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, double* partial, hipStream_t s)
 {
     auto k = k_codec<DT, DQ, ERR>;
-    const int64_t grid = persistent_grid(k, ntiles);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, tab, nl, ntiles, partial);
+    const int64_t grid = persistent_grid(k, ntiles, kCThreads);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kCThreads), 0, s, tab, nl, ntiles, partial);
     return hipGetLastError();
 }
 

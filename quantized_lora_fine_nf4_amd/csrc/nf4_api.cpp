@@ -63,7 +63,10 @@ nf4_status check_layers(const nf4_layer* L, int32_t nl, unsigned need, int64_t* 
 }
 
 size_t table_bytes(int32_t nl) { return align256(size_t(nl) * sizeof(LayerDesc)); }
-size_t partial_bytes(int64_t ntiles) { return align256(size_t(ntiles) * sizeof(double)); }
+size_t partial_bytes(int64_t ntiles)
+{
+    return align256(size_t(ntiles) * nf4k::kPartsPerTile * sizeof(double));
+}
 
 nf4_status check_ws(const void* ws, size_t ws_bytes, size_t need)
 {

@@ -10,6 +10,7 @@ namespace nf4k {
 constexpr int kTileElems = 16384;
 constexpr int kTileShift = 14;
 constexpr int kThreads = 256;
+constexpr int kPartsPerTile = 4;   // fp64 squared-error partials per tile (one per wave)
 
 // Device copy of one nf4_layer plus the running tile count: tiles of all
 // layers form one flat index space, layer l owning [tile_end - tiles(n), tile_end).
@@ -28,8 +29,8 @@ static_assert(sizeof(LayerDesc) == 64, "layer table entry is 64 bytes");
 __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileElems - 1) >> kTileShift; }
 
 // Fused blockwise quantisation (+ int8 double quantisation when dq) and, when
-// err_partial != nullptr, in-register dequantisation and per-tile fp64 squared
-// error written to err_partial[tile].
+// err_partial != nullptr, in-register dequantisation and the fp64 squared
+// error, written as kPartsPerTile partials per tile to err_partial.
 hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
                         double* err_partial, hipStream_t s);
 // Per-layer fixed-order sum of the per-tile partials into err[nl].

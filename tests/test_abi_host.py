@@ -57,7 +57,8 @@ def test_workspace_sizes():
     f = q.fmt()
     ns = [16384 * 3 + 1, 100, 64]
     tiles = 4 + 1 + 1
-    assert q.nf4_workspace_bytes(ns, f) == 256 + ((tiles * 8 + 255) // 256) * 256
+    # layer table (64 B per matrix) + 4 fp64 error partials per tile of 16384 weights
+    assert q.nf4_workspace_bytes(ns, f) == 256 + ((tiles * 4 * 8 + 255) // 256) * 256
     assert q.nf4_workspace_bytes([], f) == 0
     assert q.nf4_workspace_bytes([0], f) == 0
     assert q.aqlora_workspace_bytes(280) == 2 * 1280
