@@ -102,6 +102,63 @@ def cpu_baseline(cfg, seconds: float, n_deq: int, n_total: int):
     }
 
 
+def hbm_probe(torch):
+    """Achievable HBM streaming rates on this device with PyTorch's own kernels
+    over 8 GiB buffers (far beyond the 256 MB last-level cache): write-only
+    (fill), read+write (copy) and read-only (a max-reduction of int32)."""
+    nbytes = 8 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(7)
+    res = {}
+
+    def rate(fn, moved, reps=6):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    res["write_GBps"] = rate(lambda: b.fill_(3), nbytes)
+    res["copy_GBps"] = rate(lambda: b.copy_(a), 2 * nbytes)
+    res["read_GBps"] = rate(lambda: a.amax(), nbytes)
+    res["buffer_bytes"] = nbytes
+    return res
+
+
+def protocol_arms(launch, seconds: float, torch, stream):
+    """Fixed-duration timing with a duplicated arm: the same launch is timed as
+    arms A and A2 in alternating blocks of about 0.2 s until each has run for
+    `seconds`; returns per-arm launch durations and their relative spread."""
+    block = 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # size the block to ~0.2 s
+    e0.record(stream)
+    launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    block = max(1, int(200.0 / one))
+    tot = {"A": [0.0, 0], "A2": [0.0, 0]}
+    while min(v[0] for v in tot.values()) < seconds * 1e3:
+        for arm in ("A", "A2"):
+            e0.record(stream)
+            for _ in range(block):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot[arm][0] += e0.elapsed_time(e1)
+            tot[arm][1] += block
+    ms = {k: v[0] / v[1] for k, v in tot.items()}
+    mean = 0.5 * (ms["A"] + ms["A2"])
+    return {"ms_A": round(ms["A"], 4), "ms_A2": round(ms["A2"], 4),
+            "launches_each": tot["A"][1], "noise_floor_rel": round(abs(ms["A"] - ms["A2"]) / mean, 5)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +169,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only measure achievable streaming bandwidth with PyTorch's own kernels")
+    ap.add_argument("--protocol", type=float, default=0.0, metavar="SECONDS",
+                    help="also time each kernel for a fixed duration as two interleaved, "
+                         "identical arms (noise floor = their spread)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -135,6 +197,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
+        return
+
+    if args.hbm_probe:
+        print(json.dumps(hbm_probe(torch)), flush=True)
         return
 
     q.lib()
@@ -250,6 +316,19 @@ def main():
         "kernels": kernels,
         "source_hash": source_hash(),
     }
+    if args.protocol > 0:
+        sub = subsets[keep]
+        out["protocol"] = {
+            "seconds_per_arm": args.protocol,
+            "nf4_layer_error": protocol_arms(lambda: q.nf4_layer_error(ls, f, err, ws),
+                                             args.protocol, torch, stream),
+            "nf4_dequantize": protocol_arms(lambda: q.nf4_dequantize(sub, f, ws),
+                                            args.protocol, torch, stream),
+        }
+        for k in ("nf4_layer_error", "nf4_dequantize"):
+            pb = fused_bytes if k == "nf4_layer_error" else deq_bytes
+            pm = 0.5 * (out["protocol"][k]["ms_A"] + out["protocol"][k]["ms_A2"])
+            out["protocol"][k]["GBps"] = round(pb / (pm * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, n_deq, n_total)

@@ -38,7 +38,7 @@ constexpr int kRepl = 16;    // lane-indexed copies of the cell table: conflict-
 constexpr int kYStride = 256 + 17;   // per-block dequant table, code-major, odd pad against bank conflicts
 
 #ifndef NF4_CODEC_WAVES_PER_EU
-#define NF4_CODEC_WAVES_PER_EU 3     // at most 168 VGPRs: 3 waves per SIMD, no spills
+#define NF4_CODEC_WAVES_PER_EU 2     // no register cap below 256: no spills (issue-bound, occupancy gains nothing)
 #endif
 #ifndef NF4_DEQUANT_WAVES_PER_EU
 #define NF4_DEQUANT_WAVES_PER_EU 4
