@@ -2,8 +2,10 @@
 //
 // One tile = one double-quantisation group = 256 blocks of 64 weights
 // (16384 weights, 32 KB of bf16).  A 256-thread workgroup (4 waves) owns a
-// tile at a time and walks the flat tile index of all layers (one grouped,
-// persistent launch for the whole stack).  Lane layout: wave w, load j
+// tile at a time; the tiles of all layers form one flat index, so one grouped
+// launch covers the whole stack (persistent workgroups walking the index for
+// the fused and double-quant kernels, one workgroup per tile for the
+// standalone dequantisation).  Lane layout: wave w, load j
 // (j = 0..7), lane L reads weights w*4096 + j*512 + 8L .. +8 with one 128-bit
 // load, so each load instruction of a wave covers 1 KB contiguously and the 8
 // lanes 8m..8m+7 hold the 64 weights of one block.
@@ -40,15 +42,16 @@ constexpr int kYStride = 256 + 17;   // per-block dequant table, code-major, odd
 #ifndef NF4_CODEC_WAVES_PER_EU
 #define NF4_CODEC_WAVES_PER_EU 2     // no register cap below 256: no spills (issue-bound, occupancy gains nothing)
 #endif
-#ifndef NF4_DEQUANT_WAVES_PER_EU
-#define NF4_DEQUANT_WAVES_PER_EU 4
-#endif
 #ifndef NF4_SCHED_FENCE
 #define NF4_SCHED_FENCE 1            // scheduling fence every 8 (1) or 4 (2) weights in the fused kernel
 #endif
 #ifndef NF4_NT_STORES
 #define NF4_NT_STORES 0              // non-temporal 128-bit stores of dequantised output
 #endif
+#ifndef NF4_XCD_WALK
+#define NF4_XCD_WALK 1               // XCD-contiguous tile order within each pass of a persistent walk
+#endif
+constexpr int kXcds = 8;             // accelerator dies (XCDs), each with its own L2 and translation caches
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 128-bit load / store unit
@@ -251,6 +254,23 @@ struct TileRef {
     int valid;       // elements of the tile inside the layer (1..16384)
 };
 
+// First tile of this workgroup in a persistent walk over the flat tile index;
+// every later tile is G = gridDim.x further on, so pass k covers tiles
+// [k G, (k+1) G).  Workgroups are handed to the XCDs round-robin by index, so
+// with the identity order each XCD would own every 8th tile of a pass and its
+// translation cache would have to map the whole pass.  Giving XCD x the
+// contiguous run x G/8 .. (x+1) G/8 - 1 of every pass shrinks the span each
+// XCD touches at once eightfold.  Only the order changes, so results do not
+// depend on it; a grid that is not a multiple of 8 keeps the identity order.
+// The fused kernel, bound by its arithmetic, measures slightly faster without.
+template <bool XCD>
+__device__ __forceinline__ int64_t walk_start()
+{
+    const uint32_t b = blockIdx.x, g = gridDim.x;
+    if (!XCD || !NF4_XCD_WALK || g % kXcds) return b;
+    return (int64_t)(b % kXcds) * (g / kXcds) + b / kXcds;
+}
+
 __device__ __forceinline__ int first_layer(const LayerDesc* tab, int nl, int64_t tile)
 {
     int lo = 0, hi = nl - 1;
@@ -272,6 +292,23 @@ __device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_
     const int64_t rem = n - r.e0;
     r.valid = rem < kTileElems ? (int)rem : kTileElems;
     return r;
+}
+
+// Layer holding `tile` = the number of layers whose tile_end is <= tile
+// (tile_end grows with the layer index), found by one wave with two ballots:
+// lanes sample every s-th layer, then the s layers after the last sample that
+// ends at or before the tile.  Up to 4096 layers; beyond, the binary search.
+__device__ __forceinline__ int find_layer(const LayerDesc* tab, int nl, int64_t tile)
+{
+    if (nl > 4096) return first_layer(tab, nl, tile);
+    const int lane = threadIdx.x & 63;
+    const int s = (nl + 63) >> 6;
+    const int i = lane * s;
+    const int c = __popcll(__builtin_amdgcn_ballot_w64(i < nl && tab[i].tile_end <= tile));
+    if (s == 1 || c == 0) return c;
+    const int base = (c - 1) * s + 1;
+    const int j = base + lane;
+    return base + __popcll(__builtin_amdgcn_ballot_w64(lane < s && j < nl && tab[j].tile_end <= tile));
 }
 
 // ---- fused quantise / double-quantise / dequantise / error --------------
@@ -508,9 +545,9 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
     __shared__ CodecShared sh;
     build_cells(sh.cells);
     __syncthreads();
-    if ((int64_t)blockIdx.x >= ntiles) return;
-    int l = first_layer(tab, nl, blockIdx.x);
-    int64_t tile = blockIdx.x;
+    int64_t tile = walk_start<false>();
+    if (tile >= ntiles) return;
+    int l = first_layer(tab, nl, tile);
     TileRef tr0 = tile_ref(tab, l, tile), tr1;
     u32x4 v0[kCLoads], v1[kCLoads];
     load_tile(v0, tr0);
@@ -614,33 +651,26 @@ __device__ __forceinline__ void dequant_compute(const float* s_lv, const DqIn& r
     }
 }
 
+// One workgroup per tile: the dispatcher hands out tiles in index order, so
+// the tiles in flight stay one compact run of memory for the whole launch
+// (persistent workgroups drift apart and spread their stores).  Each wave
+// finds the layer and keeps its own copy of the level table, so the waves
+// never wait for each other.
 template <int DT, bool DQ>
-__global__ __launch_bounds__(kThreads, NF4_DEQUANT_WAVES_PER_EU) void k_dequant(
-    const LayerDesc* __restrict__ tab, int nl, int64_t ntiles)
+__global__ __launch_bounds__(kThreads) void k_dequant(const LayerDesc* __restrict__ tab, int nl,
+                                                      int64_t first_tile)
 {
-    __shared__ float s_lv[16];
-    if (threadIdx.x < 16) s_lv[threadIdx.x] = as_f(nf4fmt::kLevelBits[threadIdx.x]);
-    __syncthreads();
-    if ((int64_t)blockIdx.x >= ntiles) return;
-    int l = first_layer(tab, nl, blockIdx.x);
-    int64_t tile = blockIdx.x;
-    TileRef tr0 = tile_ref(tab, l, tile), tr1;
-    DqIn r0, r1;
-    load_dq<DQ>(r0, tr0);
-    for (;;) {
-        int64_t nxt = tile + gridDim.x;
-        bool more = nxt < ntiles;
-        if (more) { tr1 = tile_ref(tab, l, nxt); load_dq<DQ>(r1, tr1); }
-        dequant_compute<DT, DQ>(s_lv, r0, tr0);
-        if (!more) break;
-        tile = nxt;
-        nxt = tile + gridDim.x;
-        more = nxt < ntiles;
-        if (more) { tr0 = tile_ref(tab, l, nxt); load_dq<DQ>(r0, tr0); }
-        dequant_compute<DT, DQ>(s_lv, r1, tr1);
-        if (!more) break;
-        tile = nxt;
-    }
+    __shared__ float s_lv[kWaves][16];
+    const int lane = threadIdx.x & 63;
+    float* lv = s_lv[threadIdx.x >> 6];
+    if (lane < 16) lv[lane] = as_f(nf4fmt::kLevelBits[lane]);
+    const int64_t tile = first_tile + blockIdx.x;
+    int l = find_layer(tab, nl, tile);
+    const TileRef tr = tile_ref(tab, l, tile);
+    DqIn r;
+    load_dq<DQ>(r, tr);
+    __builtin_amdgcn_wave_barrier();   // the wave's table writes precede its reads (LDS keeps a wave's order)
+    dequant_compute<DT, DQ>(lv, r, tr);
 }
 
 // ---- standalone double quantisation --------------------------------------
@@ -649,10 +679,11 @@ __global__ __launch_bounds__(kThreads) void k_double_quant(const LayerDesc* __re
                                                            int nl, int64_t ntiles)
 {
     __shared__ uint32_t s_wmax[kWaves];
-    if ((int64_t)blockIdx.x >= ntiles) return;
+    const int64_t start = walk_start<true>();
+    if (start >= ntiles) return;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    int l = first_layer(tab, nl, blockIdx.x);
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int l = first_layer(tab, nl, start);
+    for (int64_t tile = start; tile < ntiles; tile += gridDim.x) {
         const TileRef tr = tile_ref(tab, l, tile);
         const LayerDesc& d = *tr.d;
         const int nbv = (tr.valid + 63) >> 6;
@@ -730,13 +761,20 @@ hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, double* partia
     return hipGetLastError();
 }
 
+// One-shot launches of at most kMaxGrid workgroups (the dispatch packet counts
+// work-items in 32 bits).
+constexpr int64_t kMaxGrid = (int64_t(1) << 32) / kThreads - 1;
+
 template <int DT, bool DQ>
 hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)
 {
-    auto k = k_dequant<DT, DQ>;
-    const int64_t grid = persistent_grid(k, ntiles);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, s, tab, nl, ntiles);
-    return hipGetLastError();
+    for (int64_t t0 = 0; t0 < ntiles; t0 += kMaxGrid) {
+        const int64_t g = ntiles - t0 < kMaxGrid ? ntiles - t0 : kMaxGrid;
+        hipLaunchKernelGGL((k_dequant<DT, DQ>), dim3((unsigned)g), dim3(kThreads), 0, s, tab, nl, t0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
