@@ -36,11 +36,20 @@ constexpr int kCWaves = kWaves;
 constexpr int kCLoads = kLoads;
 static_assert(kPartsPerTile == kCWaves, "one fp64 error partial per wave and tile");
 constexpr int kCells = 129;                              // encode cells, trunc(64 s) in [-64, 64]
-constexpr int kRepl = 16;    // lane-indexed copies of the cell table: conflict-free 64-bit reads
-constexpr int kYStride = 256 + 17;   // per-block dequant table, code-major, odd pad against bank conflicts
+#ifndef NF4_REPL
+#define NF4_REPL 16
+#endif
+#ifndef NF4_YSTRIDE
+#define NF4_YSTRIDE (256 + 17)
+#endif
+constexpr int kRepl = NF4_REPL;        // lane-indexed copies of the cell table: conflict-free 64-bit reads
+constexpr int kYStride = NF4_YSTRIDE;  // per-block dequant table, code-major, padded against bank conflicts
 
 #ifndef NF4_CODEC_WAVES_PER_EU
-#define NF4_CODEC_WAVES_PER_EU 2     // no register cap below 256: no spills (issue-bound, occupancy gains nothing)
+#define NF4_CODEC_WAVES_PER_EU 4     // schedule the fused loop for 128 VGPRs (measured fastest)
+#endif
+#ifndef NF4_CODEC_WG_PER_CU
+#define NF4_CODEC_WG_PER_CU 3        // resident fused workgroups per CU (3 measured faster than 2 or 4)
 #endif
 #ifndef NF4_SCHED_FENCE
 #define NF4_SCHED_FENCE 1            // scheduling fence every 8 (1) or 4 (2) weights in the fused kernel
@@ -338,6 +347,9 @@ struct CodecShared {
 // finite and leaves the codes unchanged), and each difference is scaled by
 // 2^k before squaring so that the fp32 squares neither underflow nor
 // overflow (exact; undone in fp64 per block, counted once per 8-lane group).
+// FULL: a whole tile (the persistent kernel); otherwise a matrix's ragged
+// last tile (the tail kernel), whose codes past the end are 0 (an odd tail's
+// high nibble) and whose bytes past the end are not written.
 template <int DT, bool ERR, bool FULL, bool SPEC>
 __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4 (&v)[kCLoads],
                                               g_u8 cp, int valid)
@@ -382,18 +394,21 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
                         e = __builtin_fmaf(dd, dd, e);
                     }
                 }
-                if constexpr (!FULL) {
-                    if (o + 2 * k2 + h >= (uint32_t)valid) code = 0;
-                }
                 pk |= code << (8 * k2 + 4 * h);
             }
         }
         if constexpr (FULL) {
             *(g_u32)(cp + (o >> 1)) = pk;
         } else {
+            const int rem = valid - (int)o;
+            if (rem >= 8) {
+                *(g_u32)(cp + (o >> 1)) = pk;
+            } else if (rem > 0) {
+                pk &= (1u << (4 * rem)) - 1u;
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-                if (o + 2 * bb < (uint32_t)valid) cp[(o >> 1) + bb] = (uint8_t)(pk >> (8 * bb));
+                for (int bb = 0; bb < 4; ++bb)
+                    if (2 * bb < rem) cp[(o >> 1) + bb] = (uint8_t)(pk >> (8 * bb));
+            }
         }
         if constexpr (ERR && SPEC) {
             const double blk_sse = __builtin_ldexp((double)sum8_f32(eb), -2 * ek);
@@ -406,32 +421,44 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
     return acc64;
 }
 
-// 1. the tile's weights into registers: 8 x 128-bit loads per lane (a ragged
-// last tile loads element by element and pads with zeros)
+// 1. the tile's weights into registers: 8 x 128-bit loads per lane.  In a
+// ragged last tile a lane loads only chunks that start inside the matrix and
+// zeroes the elements past its end.  Such a chunk is 16-byte aligned (the
+// weights are) and holds a valid element, so it lies within one mapped page;
+// the bytes past the end are read and discarded.  Padding with zeros leaves
+// every block maximum unchanged and adds nothing to the error (0 encodes to
+// level 0, which dequantises to 0).
+template <bool FULL>
 __device__ __forceinline__ void load_tile(u32x4 (&v)[kCLoads], const TileRef& tr)
 {
     const g_cu16 w = (g_cu16)tr.d->w + tr.e0;
     const int valid = tr.valid;
     const uint32_t lb = lane_base<kCThreads>();
-    if (valid == kTileElems) {
+    if constexpr (FULL) {
 #pragma unroll
         for (int j = 0; j < kCLoads; ++j) v[j] = *(g_cu4)(w + (lb + j * 512u));
     } else {
 #pragma unroll
         for (int j = 0; j < kCLoads; ++j) {
             const uint32_t o = lb + j * 512u;
-            uint16_t h[8];
+            const int rem = valid - (int)o;
+            u32x4 c = {0u, 0u, 0u, 0u};
+            if (rem > 0) {
+                c = *(g_cu4)(w + o);
+                if (rem < 8) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) h[k] = (o + k < (uint32_t)valid) ? w[o + k] : (uint16_t)0;
-            v[j].x = h[0] | ((uint32_t)h[1] << 16);
-            v[j].y = h[2] | ((uint32_t)h[3] << 16);
-            v[j].z = h[4] | ((uint32_t)h[5] << 16);
-            v[j].w = h[6] | ((uint32_t)h[7] << 16);
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t keep = rem >= 2 * k + 2 ? ~0u : (rem == 2 * k + 1 ? 0xffffu : 0u);
+                        c[k] &= keep;
+                    }
+                }
+            }
+            v[j] = c;
         }
     }
 }
 
-template <int DT, bool DQ, bool ERR>
+template <int DT, bool DQ, bool ERR, bool FULL>
 __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[kCLoads],
                                               const TileRef& tr, int64_t tile, int parity,
                                               double* __restrict__ partial)
@@ -519,13 +546,8 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 
     // 4. encode, pack, store codes; look up the dequantised values and square the error
     const g_u8 cp = (g_u8)d.codes + (tr.e0 >> 1);
-    double acc;
-    if (valid == kTileElems)
-        acc = any_spec ? encode_lane<DT, ERR, true, true>(sh, v, cp, valid)
-                       : encode_lane<DT, ERR, true, false>(sh, v, cp, valid);
-    else
-        acc = any_spec ? encode_lane<DT, ERR, false, true>(sh, v, cp, valid)
-                       : encode_lane<DT, ERR, false, false>(sh, v, cp, valid);
+    const double acc = any_spec ? encode_lane<DT, ERR, FULL, true>(sh, v, cp, valid)
+                                : encode_lane<DT, ERR, FULL, false>(sh, v, cp, valid);
 
     // 5. the wave's fp64 partial (64 lanes in a fixed order); tiles and waves
     //    are added per layer by k_reduce
@@ -537,7 +559,12 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 
 // Persistent grid-stride walk over the flat tile index, software-pipelined:
 // the next tile's loads are issued before the current tile is processed
-// (unrolled by two so the register buffers swap roles without copies).
+// (unrolled by two so the register buffers swap roles without copies).  Only
+// whole tiles are processed here; a matrix's ragged last tile is skipped by
+// the whole workgroup and left to k_codec_tail, which keeps the ragged-edge
+// code (and the registers it would hold) out of this loop.  The wave-maximum
+// buffer parity advances per processed tile: between two uses of one parity
+// the workgroup passes a barrier.
 template <int DT, bool DQ, bool ERR>
 __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
     const LayerDesc* __restrict__ tab, int nl, int64_t ntiles, double* __restrict__ partial)
@@ -550,21 +577,53 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
     int l = first_layer(tab, nl, tile);
     TileRef tr0 = tile_ref(tab, l, tile), tr1;
     u32x4 v0[kCLoads], v1[kCLoads];
-    load_tile(v0, tr0);
+    int par = 0;
+    if (tr0.valid == kTileElems) load_tile<true>(v0, tr0);
     for (;;) {
         int64_t nxt = tile + gridDim.x;
         bool more = nxt < ntiles;
-        if (more) { tr1 = tile_ref(tab, l, nxt); load_tile(v1, tr1); }
-        codec_compute<DT, DQ, ERR>(sh, v0, tr0, tile, 0, partial);
+        if (more) {
+            tr1 = tile_ref(tab, l, nxt);
+            if (tr1.valid == kTileElems) load_tile<true>(v1, tr1);
+        }
+        if (tr0.valid == kTileElems) {
+            codec_compute<DT, DQ, ERR, true>(sh, v0, tr0, tile, par, partial);
+            par ^= 1;
+        }
         if (!more) break;
         tile = nxt;
         nxt = tile + gridDim.x;
         more = nxt < ntiles;
-        if (more) { tr0 = tile_ref(tab, l, nxt); load_tile(v0, tr0); }
-        codec_compute<DT, DQ, ERR>(sh, v1, tr1, tile, 1, partial);
+        if (more) {
+            tr0 = tile_ref(tab, l, nxt);
+            if (tr0.valid == kTileElems) load_tile<true>(v0, tr0);
+        }
+        if (tr1.valid == kTileElems) {
+            codec_compute<DT, DQ, ERR, true>(sh, v1, tr1, tile, par, partial);
+            par ^= 1;
+        }
         if (!more) break;
         tile = nxt;
     }
+}
+
+// The ragged last tile of matrix blockIdx.x (n not a multiple of 16384),
+// launched after k_codec on the same stream; other workgroups exit at once.
+template <int DT, bool DQ, bool ERR>
+__global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __restrict__ tab,
+                                                          double* __restrict__ partial)
+{
+    const int64_t n = tab[blockIdx.x].n;
+    if ((n & (kTileElems - 1)) == 0) return;
+    __shared__ CodecShared sh;
+    build_cells(sh.cells);
+    __syncthreads();
+    int l = blockIdx.x;
+    const int64_t tile = tab[l].tile_end - 1;
+    const TileRef tr = tile_ref(tab, l, tile);
+    u32x4 v[kCLoads];
+    load_tile<false>(v, tr);
+    codec_compute<DT, DQ, ERR, false>(sh, v, tr, tile, 0, partial);
 }
 
 // ---- standalone dequantisation -------------------------------------------
@@ -741,23 +800,31 @@ int cu_count()
     return cus;
 }
 
+// Workgroups of a persistent launch: the resident count per CU (capped at
+// max_per_cu when given) times the CUs, at most one per tile.
 template <typename K>
-int64_t persistent_grid(K kernel, int64_t ntiles, int threads = kThreads)
+int64_t persistent_grid(K kernel, int64_t ntiles, int threads = kThreads, int max_per_cu = 0)
 {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
         per_cu <= 0)
         per_cu = 4;
+    if (max_per_cu > 0 && per_cu > max_per_cu) per_cu = max_per_cu;
     const int64_t g = (int64_t)cu_count() * per_cu;
     return ntiles < g ? ntiles : g;
 }
 
 template <int DT, bool DQ, bool ERR>
-hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, double* partial, hipStream_t s)
+hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, double* partial,
+                    hipStream_t s)
 {
     auto k = k_codec<DT, DQ, ERR>;
-    const int64_t grid = persistent_grid(k, ntiles, kCThreads);
+    const int64_t grid = persistent_grid(k, ntiles, kCThreads, NF4_CODEC_WG_PER_CU);
     hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kCThreads), 0, s, tab, nl, ntiles, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !ragged) return e;
+    hipLaunchKernelGGL((k_codec_tail<DT, DQ, ERR>), dim3((unsigned)nl), dim3(kCThreads), 0, s, tab,
+                       partial);
     return hipGetLastError();
 }
 
@@ -779,20 +846,20 @@ hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t 
 
 }  // namespace
 
-hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                        double* err_partial, hipStream_t s)
+hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, int dtype,
+                        bool dq, double* err_partial, hipStream_t s)
 {
     const bool err = err_partial != nullptr;
     if (dtype == 0) {
-        if (dq) return err ? codec_go<0, true, true>(tab, nl, ntiles, err_partial, s)
-                           : codec_go<0, true, false>(tab, nl, ntiles, nullptr, s);
-        return err ? codec_go<0, false, true>(tab, nl, ntiles, err_partial, s)
-                   : codec_go<0, false, false>(tab, nl, ntiles, nullptr, s);
+        if (dq) return err ? codec_go<0, true, true>(tab, nl, ntiles, ragged, err_partial, s)
+                           : codec_go<0, true, false>(tab, nl, ntiles, ragged, nullptr, s);
+        return err ? codec_go<0, false, true>(tab, nl, ntiles, ragged, err_partial, s)
+                   : codec_go<0, false, false>(tab, nl, ntiles, ragged, nullptr, s);
     }
-    if (dq) return err ? codec_go<1, true, true>(tab, nl, ntiles, err_partial, s)
-                       : codec_go<1, true, false>(tab, nl, ntiles, nullptr, s);
-    return err ? codec_go<1, false, true>(tab, nl, ntiles, err_partial, s)
-               : codec_go<1, false, false>(tab, nl, ntiles, nullptr, s);
+    if (dq) return err ? codec_go<1, true, true>(tab, nl, ntiles, ragged, err_partial, s)
+                       : codec_go<1, true, false>(tab, nl, ntiles, ragged, nullptr, s);
+    return err ? codec_go<1, false, true>(tab, nl, ntiles, ragged, err_partial, s)
+               : codec_go<1, false, false>(tab, nl, ntiles, ragged, nullptr, s);
 }
 
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,

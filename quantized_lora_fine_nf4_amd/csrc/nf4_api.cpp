@@ -62,6 +62,14 @@ nf4_status check_layers(const nf4_layer* L, int32_t nl, unsigned need, int64_t* 
     return NF4_OK;
 }
 
+// Some matrix ends in a partial tile (the fused pass then adds its tail launch).
+bool any_ragged(const nf4_layer* L, int32_t nl)
+{
+    for (int32_t i = 0; i < nl; ++i)
+        if (L[i].n % nf4k::kTileElems) return true;
+    return false;
+}
+
 size_t table_bytes(int32_t nl) { return align256(size_t(nl) * sizeof(LayerDesc)); }
 size_t partial_bytes(int64_t ntiles)
 {
@@ -172,8 +180,8 @@ nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, voi
     if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
-    hipError_t e = nf4k::launch_codec(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype, dq,
-                                      nullptr, s);
+    hipError_t e = nf4k::launch_codec(static_cast<const LayerDesc*>(ws), nl, ntiles,
+                                      any_ragged(layers, nl), fmt.dtype, dq, nullptr, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
@@ -229,7 +237,8 @@ nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt, 
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     const LayerDesc* tab = static_cast<const LayerDesc*>(ws);
     double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + table_bytes(nl));
-    hipError_t e = nf4k::launch_codec(tab, nl, ntiles, fmt.dtype, dq, partial, s);
+    hipError_t e = nf4k::launch_codec(tab, nl, ntiles, any_ragged(layers, nl), fmt.dtype, dq,
+                                      partial, s);
     if (e != hipSuccess) return hip_fail(e);
     e = nf4k::launch_reduce(tab, nl, partial, err, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);

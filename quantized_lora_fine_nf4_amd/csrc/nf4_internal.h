@@ -30,9 +30,10 @@ __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileElems 
 
 // Fused blockwise quantisation (+ int8 double quantisation when dq) and, when
 // err_partial != nullptr, in-register dequantisation and the fp64 squared
-// error, written as kPartsPerTile partials per tile to err_partial.
-hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                        double* err_partial, hipStream_t s);
+// error, written as kPartsPerTile partials per tile to err_partial.  ragged:
+// some layer's n is not a multiple of kTileElems (adds the tail launch).
+hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, int dtype,
+                        bool dq, double* err_partial, hipStream_t s);
 // Per-layer fixed-order sum of the per-tile partials into err[nl].
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
                          hipStream_t s);
