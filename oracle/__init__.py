@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "nf4o_storage_bytes": (i64, [i64, i32]),
             "nf4o_promote_cost": (i64, [i64, i32]),
             "nf4o_select_topk": (i32, [P, P, i32, i64, i32, P]),
+            "nf4o_sumsq": (ctypes.c_double, [P, i64, i32]),
+            "nf4o_select": (i32, [P, P, P, i32, P, i32, i64, i32, i32, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -187,4 +189,27 @@ def select_topk(err, cost, budget: int = -1, kcap: int = -1):
     nl = err.size
     sel = np.zeros(nl, np.uint8)
     K = lib().nf4o_select_topk(_p(err), _p(cost), nl, int(budget), int(kcap), _p(sel))
+    return sel, K
+
+
+def sumsq(w: np.ndarray, dtype: int) -> float:
+    """Sum of x^2 over a 16-bit matrix, fp64."""
+    w = np.ascontiguousarray(w, np.uint16).ravel()
+    return lib().nf4o_sumsq(_p(w), w.size, dtype)
+
+
+PREFIX, FILL = 0, 1
+
+
+def select(err, cost, budget: int = -1, kcap: int = -1, denom=None, group_end=None,
+           rule: int = PREFIX):
+    """General selection -> (selected[nl] u8, units taken)."""
+    err = np.ascontiguousarray(err, np.float64)
+    cost = np.ascontiguousarray(cost, np.int64)
+    nl = err.size
+    d = None if denom is None else np.ascontiguousarray(denom, np.float64)
+    g = None if group_end is None else np.ascontiguousarray(group_end, np.int32)
+    sel = np.zeros(nl, np.uint8)
+    K = lib().nf4o_select(_p(err), _p(d), _p(cost), nl, _p(g), 0 if g is None else g.size,
+                          int(budget), int(kcap), int(rule), _p(sel))
     return sel, K

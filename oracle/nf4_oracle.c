@@ -376,3 +376,89 @@ int nf4o_select_topk(const double* err, const int64_t* cost, int nl,
     free(order);
     return K;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Selection variants (scores, budget rule, granularity).                     */
+/* ------------------------------------------------------------------------- */
+/* Squared norm of a matrix, sum of x^2 in fp64 with Neumaier compensation:
+ * the denominator of the relative score SSE / ||W||^2.  [AQLoRA abstract]
+ * ranks by reconstruction error without saying whether it is normalised;
+ * the normalised forms are variants of that score. */
+double nf4o_sumsq(const uint16_t* w, int64_t n, int dtype)
+{
+    double sum = 0.0, comp = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double x = (double)nf4o_from16(w[i], dtype);
+        double t = x * x;
+        double s = sum + t;
+        if (fabs(sum) >= fabs(t)) comp += (sum - s) + t;
+        else                      comp += (t - s) + sum;
+        sum = s;
+    }
+    return sum + comp;
+}
+
+/* [AQLoRA abstract] keeps the top-K under a memory budget; a speed setting
+ * adapts only the top blocks.  Readings of the variants:
+ *   score of layer i = err[i] / denom[i] when denom is given (denom = n gives
+ *     the mean squared error, denom = sum of squares the relative error), else
+ *     err[i]; the division is IEEE fp64;
+ *   units: single layers, or groups of consecutive layers (group g = layers
+ *     group_end[g-1] .. group_end[g]-1, group_end[-1] = 0), a group's score
+ *     being the sum of its layers' scores in layer order and its cost the sum
+ *     of their costs -- a transformer block promoted as a whole;
+ *   order: score descending, equal scores by unit index ascending;
+ *   rule 0 (prefix): take units in that order, stop at the first that would
+ *     take the running cost over the budget;
+ *   rule 1 (fill): take every unit, in that order, that still fits, skipping
+ *     the ones that do not;
+ *   at most kcap units (kcap < 0: no cap); budget < 0: no byte budget.
+ * Writes selected[nl] per layer and returns the number of units taken. */
+int nf4o_select(const double* err, const double* denom, const int64_t* cost, int nl,
+                const int32_t* group_end, int ngroups, int64_t budget, int kcap, int rule,
+                uint8_t* selected)
+{
+    const int nu = group_end ? ngroups : nl;
+    rank_item* order = (rank_item*)malloc(sizeof(rank_item) * (size_t)(nu > 0 ? nu : 1));
+    int64_t* ucost = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nu > 0 ? nu : 1));
+    uint8_t* take = (uint8_t*)calloc((size_t)(nu > 0 ? nu : 1), 1);
+    for (int u = 0; u < nu; ++u) {
+        int b = group_end ? (u ? group_end[u - 1] : 0) : u;
+        int e = group_end ? group_end[u] : u + 1;
+        double score = 0.0;
+        int64_t c = 0;
+        for (int i = b; i < e; ++i) {
+            double s = denom ? err[i] / denom[i] : err[i];
+            assert(!isnan(s));
+            score += s;
+            c += cost[i];
+        }
+        order[u].err = score;
+        order[u].idx = u;
+        ucost[u] = c;
+    }
+    qsort(order, (size_t)nu, sizeof(rank_item), rank_cmp);
+    int K = 0;
+    int64_t total = 0;
+    for (int r = 0; r < nu; ++r) {
+        if (kcap >= 0 && K >= kcap) break;
+        int u = order[r].idx;
+        int64_t next = total + ucost[u];
+        if (budget >= 0 && next > budget) {
+            if (rule == 0) break;
+            continue;
+        }
+        total = next;
+        take[u] = 1;
+        ++K;
+    }
+    for (int u = 0; u < nu; ++u) {
+        int b = group_end ? (u ? group_end[u - 1] : 0) : u;
+        int e = group_end ? group_end[u] : u + 1;
+        for (int i = b; i < e; ++i) selected[i] = take[u];
+    }
+    free(order);
+    free(ucost);
+    free(take);
+    return K;
+}

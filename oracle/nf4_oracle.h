@@ -81,6 +81,16 @@ int64_t  nf4o_promote_cost(int64_t n, int dq);
 int      nf4o_select_topk(const double* err, const int64_t* cost, int nl,
                           int64_t budget, int kcap, uint8_t* selected);
 
+/* Selection variants.  Sum of x^2 over a matrix in fp64 (the relative score's
+ * denominator), and the general selection: optional per-layer divisor of the
+ * error, optional groups of consecutive layers (group_end[g] = one past the
+ * group's last layer), rule 0 = stop at the first unit that does not fit,
+ * rule 1 = skip it and keep filling.  Returns the number of units taken. */
+double   nf4o_sumsq(const uint16_t* w, int64_t n, int dtype);
+int      nf4o_select(const double* err, const double* denom, const int64_t* cost, int nl,
+                     const int32_t* group_end, int ngroups, int64_t budget, int kcap,
+                     int rule, uint8_t* selected);
+
 #ifdef __cplusplus
 }
 #endif
