@@ -140,6 +140,51 @@ def hbm_probe(torch):
     return res
 
 
+def variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes, reps=10):
+    """Selection variants on the same stack, after the timed steps: the fused
+    pass that also returns the sum of squares (relative scores), and the
+    selector with relative scores, transformer-block units and both budget
+    rules.  Mean launch time from events on the launch stream."""
+    nl = cfg.n_layers
+
+    def timed(fn):
+        fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            e[2 * r].record(stream)
+            fn()
+            e[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[2 * r].elapsed_time(e[2 * r + 1]) for r in range(reps)) / reps
+
+    sq = torch.empty_like(err)
+    res = {}
+    t_plain = timed(lambda: q.nf4_layer_error(ls, f, err, ws))
+    t_norm = timed(lambda: q.nf4_layer_error_norm(ls, f, err, sq, ws))
+    res["nf4_layer_error_ms"] = round(t_plain, 4)
+    res["nf4_layer_error_norm_ms"] = round(t_norm, 4)
+    res["nf4_layer_error_norm_GBps"] = round(fused_bytes / (t_norm * 1e-3) / 1e9, 1)
+    m = len(cfg.per_block)
+    ge = list(range(m, nl + 1, m))
+    sws = torch.empty(q.aqlora_workspace_bytes(nl), dtype=torch.uint8, device="cuda")
+    sel = torch.empty(nl, dtype=torch.uint8, device="cuda")
+    k = torch.empty(1, dtype=torch.int32, device="cuda")
+    sel_us = {}
+    for name, kw in (("topk", None),
+                     ("relative_prefix", dict(denom=sq)),
+                     ("relative_fill", dict(denom=sq, rule=q.AQLORA_FILL)),
+                     ("blocks_prefix", dict(group_end=ge)),
+                     ("relative_blocks_fill", dict(denom=sq, group_end=ge, rule=q.AQLORA_FILL))):
+        if kw is None:
+            fn = lambda: q.aqlora_select_topk(err, cost, budget, cfg.kcap, sel, k, sws)
+        else:
+            fn = lambda kw=kw: q.aqlora_select(err, cost, budget, cfg.kcap, sel, k, sws, **kw)
+        sel_us[name] = round(timed(fn) * 1e3, 1)
+    res["select_us"] = sel_us
+    res["select_layers"] = nl
+    return res
+
+
 def protocol_arms(launch, seconds: float, torch, stream):
     """Fixed-duration timing with a duplicated arm: the same launch is timed as
     arms A and A2 in alternating blocks of about 0.2 s until each has run for
@@ -177,6 +222,8 @@ def main():
     ap.add_argument("--config", default="14b", help="toy | single | 1.4b | 7b | 14b")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the selection variants after the steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -326,6 +373,8 @@ def main():
         "kernels": kernels,
         "source_hash": source_hash(),
     }
+    if not args.no_variants:
+        out["variants"] = variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes)
     if args.protocol > 0:
         sub = subsets[keep]
         out["protocol"] = {

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NF4_ABI_VERSION 1
+#define NF4_ABI_VERSION 2
 
 typedef enum {
     NF4_OK = 0,
@@ -84,6 +84,12 @@ typedef enum {
 } nf4_status;
 
 typedef enum { NF4_BF16 = 0, NF4_FP16 = 1 } nf4_dtype;
+
+/* Budget rules of aqlora_select. */
+typedef enum {
+    AQLORA_PREFIX = 0,  /* take units in rank order, stop at the first that does not fit */
+    AQLORA_FILL = 1     /* take every unit, in rank order, that still fits               */
+} aqlora_rule;
 
 typedef struct {
     int32_t dtype;      /* nf4_dtype of the 16-bit weights (and of dequantised output)  */
@@ -131,6 +137,18 @@ nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
 nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                            double* err, void* ws, size_t ws_bytes, void* stream);
 
+/* nf4_layer_error plus sumsq[nl] (device fp64): the sum of x^2 over each
+ * matrix, the denominator of the relative score err / sumsq.  The pages rank
+ * by reconstruction error without fixing a normalisation ("AQLoRA" arXiv
+ * listing, English abstract); the normalised scores are variants of that
+ * score.  Same precision and order as err (fp32 over each lane's 64 weights,
+ * fp64 beyond); err is bitwise the same as nf4_layer_error's.  The same pass,
+ * about one more instruction per weight.  sumsq must be non-NULL, 8-byte
+ * aligned. */
+nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                                double* err, double* sumsq, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Budgeted top-K over per-layer scores, on the device.
  *   err[nl]   device fp64 scores (finite, as written by nf4_layer_error)
  *   cost[nl]  device int64 promotion costs (aqlora_promote_cost)
@@ -143,11 +161,41 @@ nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl
                               uint8_t* selected, int32_t* k_out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* Selection variants on the device.  The pages keep the top-K layers under a
+ * memory budget, and their speed setting adapts only the top blocks
+ * ("AQLoRA" arXiv listing, English abstract; "AQLoRA: A Zero-Search
+ * Recipe...", Technical Details); the options read those words:
+ *   denom[nl]   device fp64 or NULL: layer i scores err[i] / denom[i] (IEEE
+ *               fp64), e.g. n for the mean squared error, sumsq from
+ *               nf4_layer_error_norm for the relative error; each > 0 and
+ *               finite, else the scores are unspecified.  NULL: err[i].
+ *   group_end   HOST int32[ngroups] or NULL: units are groups of consecutive
+ *               layers (group g = layers group_end[g-1] .. group_end[g]-1,
+ *               group_end[-1] = 0; strictly increasing, last == nl), e.g. the
+ *               matrices of each transformer block, scored by the sum of their
+ *               layers' scores in layer order and costed by the sum of their
+ *               costs, and promoted whole.  Copied before the call returns.
+ *               NULL: units are single layers (ngroups ignored).
+ *   rule        AQLORA_PREFIX or AQLORA_FILL.
+ * Units are ranked by score descending, equal scores by unit index ascending;
+ * k_cap (< 0: none) caps the number of units, budget_bytes (< 0: none) their
+ * total cost.  Writes selected[nl] per layer (1 = promoted) and k_out = the
+ * number of units taken.  With denom and group_end NULL and AQLORA_PREFIX
+ * this is aqlora_select_topk.  1 <= nl <= 65536; bad group_end or rule:
+ * NF4_E_ARG; ws of aqlora_workspace_bytes(nl). */
+nf4_status aqlora_select(const double* err, const double* denom, const int64_t* cost,
+                         int32_t nl, const int32_t* group_end, int32_t ngroups,
+                         int64_t budget_bytes, int32_t k_cap, int32_t rule,
+                         uint8_t* selected, int32_t* k_out,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* ---- host-only helpers (pure; no HIP calls) ---- */
 
-/* Workspace for every codec call above over these matrices; 0 on bad input. */
+/* Workspace for every codec call above over these matrices (the descriptor
+ * table plus two arrays of 4 fp64 partials per 16384-weight tile); 0 on bad
+ * input. */
 size_t      nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format fmt);
-/* Workspace for aqlora_select_topk; 0 on bad input. */
+/* Workspace for aqlora_select_topk and aqlora_select; 0 on bad input. */
 size_t      aqlora_workspace_bytes(int32_t nl);
 /* ceil(n/2) + (dq_group ? nb + 4*ng : 4*nb); -1 on bad input. */
 int64_t     nf4_storage_bytes(int64_t n, nf4_format fmt);

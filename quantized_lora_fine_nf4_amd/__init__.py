@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_PKG, "libnf4.so")
 
 NF4_OK, NF4_E_ARG, NF4_E_ALIGN, NF4_E_UNSUPPORTED, NF4_E_WORKSPACE, NF4_E_HIP = range(6)
 NF4_BF16, NF4_FP16 = 0, 1
+AQLORA_PREFIX, AQLORA_FILL = 0, 1
 BLOCK, DQ_GROUP = 64, 256
 
 
@@ -63,10 +64,18 @@ EXPORTS = {
     "nf4_layer_error": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]),
+    "nf4_layer_error_norm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
     "aqlora_select_topk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.c_void_p]),
+    "aqlora_select": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]),
     "nf4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32, nf4_format]),
     "aqlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
     "nf4_storage_bytes": (ctypes.c_int64, [ctypes.c_int64, nf4_format]),
@@ -165,6 +174,26 @@ def aqlora_select_topk(err, cost, budget_bytes: int, k_cap: int, selected, k_out
                                     _ptr(selected), _ptr(k_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)),
            "aqlora_select_topk")
+
+
+def nf4_layer_error_norm(layers, f: nf4_format, err, sumsq, ws, stream=None) -> None:
+    arr, nl = _layers_arg(layers)
+    _check(lib().nf4_layer_error_norm(arr, nl, f, _ptr(err), _ptr(sumsq), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "nf4_layer_error_norm")
+
+
+def aqlora_select(err, cost, budget_bytes: int, k_cap: int, selected, k_out, ws, denom=None,
+                  group_end=None, rule: int = AQLORA_PREFIX, stream=None) -> None:
+    """group_end: host sequence of group ends (copied before return), or None."""
+    nl = int(err.numel())
+    ge = None if group_end is None else np.ascontiguousarray(group_end, np.int32)
+    _check(lib().aqlora_select(_ptr(err), _ptr(denom), _ptr(cost), nl,
+                               None if ge is None else ge.ctypes.data,
+                               0 if ge is None else int(ge.size), int(budget_bytes), int(k_cap),
+                               int(rule), _ptr(selected), _ptr(k_out), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)),
+           "aqlora_select")
 
 
 # ---- host helpers ---------------------------------------------------------

@@ -350,15 +350,22 @@ struct CodecShared {
 // FULL: a whole tile (the persistent kernel); otherwise a matrix's ragged
 // last tile (the tail kernel), whose codes past the end are 0 (an odd tail's
 // high nibble) and whose bytes past the end are not written.
-template <int DT, bool ERR, bool FULL, bool SPEC>
-__device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4 (&v)[kCLoads],
-                                              g_u8 cp, int valid)
+// NORM (with ERR): also the sum of x^2 over the lane's weights, in the same
+// precision and with the same 2^k scaling as the error.
+struct LaneSums {
+    double err;
+    double sq;
+};
+
+template <int DT, bool ERR, bool NORM, bool FULL, bool SPEC>
+__device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
+                                                const u32x4 (&v)[kCLoads], g_u8 cp, int valid)
 {
     const int lane = threadIdx.x & 63;
     const EncCell* cells = sh.cells + (lane & (kRepl - 1));
     const uint32_t lb = lane_base<kCThreads>();
-    float e = 0.0f;
-    double acc64 = 0.0;
+    float e = 0.0f, q = 0.0f;
+    double acc64 = 0.0, sq64 = 0.0;
 #pragma unroll
     for (int j = 0; j < kCLoads; ++j) {
         const uint32_t o = lb + j * 512u;
@@ -372,7 +379,7 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
         }
         const uint32_t dw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t pk = 0;
-        float eb = 0.0f;
+        float eb = 0.0f, qb = 0.0f;
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {
 #if NF4_SCHED_FENCE == 2
@@ -392,6 +399,14 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
                         eb = __builtin_fmaf(dd, dd, eb);
                     } else {
                         e = __builtin_fmaf(dd, dd, e);
+                    }
+                }
+                if constexpr (NORM) {
+                    if constexpr (SPEC) {
+                        const float xs = __builtin_amdgcn_ldexpf(x[h], ek);
+                        qb = __builtin_fmaf(xs, xs, qb);
+                    } else {
+                        q = __builtin_fmaf(x[h], x[h], q);
                     }
                 }
                 pk |= code << (8 * k2 + 4 * h);
@@ -414,11 +429,16 @@ __device__ __forceinline__ double encode_lane(const CodecShared& sh, const u32x4
             const double blk_sse = __builtin_ldexp((double)sum8_f32(eb), -2 * ek);
             if ((lane & 7) == 0) acc64 += blk_sse;
         }
+        if constexpr (NORM && SPEC) {
+            const double blk_sq = __builtin_ldexp((double)sum8_f32(qb), -2 * ek);
+            if ((lane & 7) == 0) sq64 += blk_sq;
+        }
         // keep the scheduler from hoisting the next group's lookups (register pressure)
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (ERR && !SPEC) acc64 = (double)e;
-    return acc64;
+    if constexpr (NORM && !SPEC) sq64 = (double)q;
+    return LaneSums{acc64, sq64};
 }
 
 // 1. the tile's weights into registers: 8 x 128-bit loads per lane.  In a
@@ -458,10 +478,11 @@ __device__ __forceinline__ void load_tile(u32x4 (&v)[kCLoads], const TileRef& tr
     }
 }
 
-template <int DT, bool DQ, bool ERR, bool FULL>
+template <int DT, bool DQ, bool ERR, bool NORM, bool FULL>
 __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[kCLoads],
                                               const TileRef& tr, int64_t tile, int parity,
-                                              double* __restrict__ partial)
+                                              double* __restrict__ partial,
+                                              double* __restrict__ partial_sq)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const LayerDesc& d = *tr.d;
@@ -546,14 +567,18 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 
     // 4. encode, pack, store codes; look up the dequantised values and square the error
     const g_u8 cp = (g_u8)d.codes + (tr.e0 >> 1);
-    const double acc = any_spec ? encode_lane<DT, ERR, FULL, true>(sh, v, cp, valid)
-                                : encode_lane<DT, ERR, FULL, false>(sh, v, cp, valid);
+    const LaneSums acc = any_spec ? encode_lane<DT, ERR, NORM, FULL, true>(sh, v, cp, valid)
+                                  : encode_lane<DT, ERR, NORM, FULL, false>(sh, v, cp, valid);
 
     // 5. the wave's fp64 partial (64 lanes in a fixed order); tiles and waves
     //    are added per layer by k_reduce
     if constexpr (ERR) {
-        const double acc64 = wave_sum_f64(acc);
+        const double acc64 = wave_sum_f64(acc.err);
         if (lane == 0) partial[tile * kPartsPerTile + wv] = acc64;
+    }
+    if constexpr (NORM) {
+        const double sq64 = wave_sum_f64(acc.sq);
+        if (lane == 0) partial_sq[tile * kPartsPerTile + wv] = sq64;
     }
 }
 
@@ -565,9 +590,10 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 // code (and the registers it would hold) out of this loop.  The wave-maximum
 // buffer parity advances per processed tile: between two uses of one parity
 // the workgroup passes a barrier.
-template <int DT, bool DQ, bool ERR>
+template <int DT, bool DQ, bool ERR, bool NORM>
 __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
-    const LayerDesc* __restrict__ tab, int nl, int64_t ntiles, double* __restrict__ partial)
+    const LayerDesc* __restrict__ tab, int nl, int64_t ntiles, double* __restrict__ partial,
+    double* __restrict__ partial_sq)
 {
     __shared__ CodecShared sh;
     build_cells(sh.cells);
@@ -587,7 +613,7 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
             if (tr1.valid == kTileElems) load_tile<true>(v1, tr1);
         }
         if (tr0.valid == kTileElems) {
-            codec_compute<DT, DQ, ERR, true>(sh, v0, tr0, tile, par, partial);
+            codec_compute<DT, DQ, ERR, NORM, true>(sh, v0, tr0, tile, par, partial, partial_sq);
             par ^= 1;
         }
         if (!more) break;
@@ -599,7 +625,7 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
             if (tr0.valid == kTileElems) load_tile<true>(v0, tr0);
         }
         if (tr1.valid == kTileElems) {
-            codec_compute<DT, DQ, ERR, true>(sh, v1, tr1, tile, par, partial);
+            codec_compute<DT, DQ, ERR, NORM, true>(sh, v1, tr1, tile, par, partial, partial_sq);
             par ^= 1;
         }
         if (!more) break;
@@ -609,9 +635,10 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
 
 // The ragged last tile of matrix blockIdx.x (n not a multiple of 16384),
 // launched after k_codec on the same stream; other workgroups exit at once.
-template <int DT, bool DQ, bool ERR>
+template <int DT, bool DQ, bool ERR, bool NORM>
 __global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __restrict__ tab,
-                                                          double* __restrict__ partial)
+                                                          double* __restrict__ partial,
+                                                          double* __restrict__ partial_sq)
 {
     const int64_t n = tab[blockIdx.x].n;
     if ((n & (kTileElems - 1)) == 0) return;
@@ -623,7 +650,7 @@ __global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __res
     const TileRef tr = tile_ref(tab, l, tile);
     u32x4 v[kCLoads];
     load_tile<false>(v, tr);
-    codec_compute<DT, DQ, ERR, false>(sh, v, tr, tile, 0, partial);
+    codec_compute<DT, DQ, ERR, NORM, false>(sh, v, tr, tile, 0, partial, partial_sq);
 }
 
 // ---- standalone dequantisation -------------------------------------------
@@ -814,17 +841,18 @@ int64_t persistent_grid(K kernel, int64_t ntiles, int threads = kThreads, int ma
     return ntiles < g ? ntiles : g;
 }
 
-template <int DT, bool DQ, bool ERR>
+template <int DT, bool DQ, bool ERR, bool NORM>
 hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, double* partial,
-                    hipStream_t s)
+                    double* partial_sq, hipStream_t s)
 {
-    auto k = k_codec<DT, DQ, ERR>;
+    auto k = k_codec<DT, DQ, ERR, NORM>;
     const int64_t grid = persistent_grid(k, ntiles, kCThreads, NF4_CODEC_WG_PER_CU);
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kCThreads), 0, s, tab, nl, ntiles, partial);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kCThreads), 0, s, tab, nl, ntiles, partial,
+                       partial_sq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !ragged) return e;
-    hipLaunchKernelGGL((k_codec_tail<DT, DQ, ERR>), dim3((unsigned)nl), dim3(kCThreads), 0, s, tab,
-                       partial);
+    hipLaunchKernelGGL((k_codec_tail<DT, DQ, ERR, NORM>), dim3((unsigned)nl), dim3(kCThreads), 0, s,
+                       tab, partial, partial_sq);
     return hipGetLastError();
 }
 
@@ -847,19 +875,17 @@ hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t 
 }  // namespace
 
 hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, int dtype,
-                        bool dq, double* err_partial, hipStream_t s)
+                        bool dq, double* err_partial, double* sq_partial, hipStream_t s)
 {
-    const bool err = err_partial != nullptr;
-    if (dtype == 0) {
-        if (dq) return err ? codec_go<0, true, true>(tab, nl, ntiles, ragged, err_partial, s)
-                           : codec_go<0, true, false>(tab, nl, ntiles, ragged, nullptr, s);
-        return err ? codec_go<0, false, true>(tab, nl, ntiles, ragged, err_partial, s)
-                   : codec_go<0, false, false>(tab, nl, ntiles, ragged, nullptr, s);
-    }
-    if (dq) return err ? codec_go<1, true, true>(tab, nl, ntiles, ragged, err_partial, s)
-                       : codec_go<1, true, false>(tab, nl, ntiles, ragged, nullptr, s);
-    return err ? codec_go<1, false, true>(tab, nl, ntiles, ragged, err_partial, s)
-               : codec_go<1, false, false>(tab, nl, ntiles, ragged, nullptr, s);
+    // err_partial: the error; sq_partial (only with err_partial): also the sum of squares
+    const int mode = !err_partial ? 0 : (!sq_partial ? 1 : 2);
+#define NF4_CODEC_GO(DT, DQ)                                                                     \
+    (mode == 0 ? codec_go<DT, DQ, false, false>(tab, nl, ntiles, ragged, nullptr, nullptr, s)   \
+     : mode == 1 ? codec_go<DT, DQ, true, false>(tab, nl, ntiles, ragged, err_partial, nullptr, s) \
+                 : codec_go<DT, DQ, true, true>(tab, nl, ntiles, ragged, err_partial, sq_partial, s))
+    if (dtype == 0) return dq ? NF4_CODEC_GO(0, true) : NF4_CODEC_GO(0, false);
+    return dq ? NF4_CODEC_GO(1, true) : NF4_CODEC_GO(1, false);
+#undef NF4_CODEC_GO
 }
 
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,

@@ -106,6 +106,58 @@ nf4_status stage_table(const nf4_layer* L, int32_t nl, void* ws, hipStream_t s)
     return NF4_OK;
 }
 
+// The fused pass; with sumsq also the per-layer sum of x^2 (partials for it
+// follow the error partials in the workspace).
+nf4_status layer_error_impl(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
+                            double* sumsq, void* ws, size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    const bool dq = fmt.dq_group != 0;
+    if (!err) return NF4_E_ARG;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl,
+                      NEED_W | NEED_CODES | (dq ? NEED_Q | NEED_S2 | OPT_ABSMAX : NEED_ABSMAX),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if (!aligned(err, 8) || (sumsq && !aligned(sumsq, 8))) return NF4_E_ALIGN;
+    const size_t need = table_bytes(nl) + (sumsq ? 2 : 1) * partial_bytes(ntiles);
+    if ((st = check_ws(ws, ws_bytes, need)) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
+    const LayerDesc* tab = static_cast<const LayerDesc*>(ws);
+    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + table_bytes(nl));
+    double* partial_sq = sumsq ? reinterpret_cast<double*>(reinterpret_cast<char*>(partial) +
+                                                           partial_bytes(ntiles))
+                               : nullptr;
+    hipError_t e = nf4k::launch_codec(tab, nl, ntiles, any_ragged(layers, nl), fmt.dtype, dq,
+                                      partial, partial_sq, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = nf4k::launch_reduce(tab, nl, partial, err, s);
+    if (e == hipSuccess && sumsq) e = nf4k::launch_reduce(tab, nl, partial_sq, sumsq, s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+// Selection workspace: rank, perm (as aqlora_select_topk uses them), then the
+// staged group boundaries, unit scores, unit costs and unit flags.
+struct SelectLayout {
+    size_t rank, perm, groups, uscore, ucost, flag, total;
+};
+
+SelectLayout select_layout(int32_t nl)
+{
+    SelectLayout L;
+    const size_t i4 = align256(size_t(nl) * 4), i8 = align256(size_t(nl) * 8);
+    L.rank = 0;
+    L.perm = L.rank + i4;
+    L.groups = L.perm + i4;
+    L.uscore = L.groups + i4;
+    L.ucost = L.uscore + i8;
+    L.flag = L.ucost + i8;
+    L.total = L.flag + align256(size_t(nl));
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,13 +210,13 @@ size_t nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format f)
         if (n_per_layer[i] <= 0 || n_per_layer[i] >= kMaxN) return 0;
         ntiles += nf4k::tiles_of(n_per_layer[i]);
     }
-    return table_bytes(nl) + partial_bytes(ntiles);
+    return table_bytes(nl) + 2 * partial_bytes(ntiles);   // error and sum-of-squares partials
 }
 
 size_t aqlora_workspace_bytes(int32_t nl)
 {
     if (nl <= 0 || nl > kMaxSelectLayers) return 0;
-    return 2 * align256(size_t(nl) * sizeof(int32_t));
+    return select_layout(nl).total;
 }
 
 nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
@@ -181,7 +233,7 @@ nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_codec(static_cast<const LayerDesc*>(ws), nl, ntiles,
-                                      any_ragged(layers, nl), fmt.dtype, dq, nullptr, s);
+                                      any_ragged(layers, nl), fmt.dtype, dq, nullptr, nullptr, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
@@ -222,26 +274,14 @@ nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, v
 nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
                            void* ws, size_t ws_bytes, void* stream)
 {
-    nf4_status st = check_format(fmt);
-    if (st != NF4_OK) return st;
-    const bool dq = fmt.dq_group != 0;
-    if (!err) return NF4_E_ARG;
-    int64_t ntiles = 0;
-    st = check_layers(layers, nl,
-                      NEED_W | NEED_CODES | (dq ? NEED_Q | NEED_S2 | OPT_ABSMAX : NEED_ABSMAX),
-                      &ntiles);
-    if (st != NF4_OK) return st;
-    if (!aligned(err, 8)) return NF4_E_ALIGN;
-    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + partial_bytes(ntiles))) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
-    const LayerDesc* tab = static_cast<const LayerDesc*>(ws);
-    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + table_bytes(nl));
-    hipError_t e = nf4k::launch_codec(tab, nl, ntiles, any_ragged(layers, nl), fmt.dtype, dq,
-                                      partial, s);
-    if (e != hipSuccess) return hip_fail(e);
-    e = nf4k::launch_reduce(tab, nl, partial, err, s);
-    return e == hipSuccess ? NF4_OK : hip_fail(e);
+    return layer_error_impl(layers, nl, fmt, err, nullptr, ws, ws_bytes, stream);
+}
+
+nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
+                                double* sumsq, void* ws, size_t ws_bytes, void* stream)
+{
+    if (!sumsq) return NF4_E_ARG;
+    return layer_error_impl(layers, nl, fmt, err, sumsq, ws, ws_bytes, stream);
 }
 
 nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl,
@@ -258,6 +298,47 @@ nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl
                                                align256(size_t(nl) * sizeof(int32_t)));
     hipError_t e = nf4k::launch_select(err, cost, nl, budget_bytes, k_cap, selected, k_out, rank,
                                        perm, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+nf4_status aqlora_select(const double* err, const double* denom, const int64_t* cost, int32_t nl,
+                         const int32_t* group_end, int32_t ngroups, int64_t budget_bytes,
+                         int32_t k_cap, int32_t rule, uint8_t* selected, int32_t* k_out,
+                         void* ws, size_t ws_bytes, void* stream)
+{
+    if (!err || !cost || !selected || !k_out) return NF4_E_ARG;
+    if (nl <= 0 || nl > kMaxSelectLayers) return NF4_E_ARG;
+    if (rule != AQLORA_PREFIX && rule != AQLORA_FILL) return NF4_E_ARG;
+    if (group_end) {
+        if (ngroups <= 0 || ngroups > nl || group_end[ngroups - 1] != nl) return NF4_E_ARG;
+        int32_t prev = 0;
+        for (int32_t g = 0; g < ngroups; ++g) {
+            if (group_end[g] <= prev) return NF4_E_ARG;
+            prev = group_end[g];
+        }
+    }
+    if (!aligned(err, 8) || !aligned(cost, 8) || !aligned(k_out, 4) || (denom && !aligned(denom, 8)))
+        return NF4_E_ALIGN;
+    const SelectLayout L = select_layout(nl);
+    nf4_status st = check_ws(ws, ws_bytes, L.total);
+    if (st != NF4_OK) return st;
+    char* w = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* ge = nullptr;
+    if (group_end) {
+        // pageable source: staged by the runtime before the call returns
+        ge = reinterpret_cast<int32_t*>(w + L.groups);
+        hipError_t e = hipMemcpyAsync(ge, group_end, sizeof(int32_t) * size_t(ngroups),
+                                      hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    nf4k::SelectScratch scr{reinterpret_cast<int32_t*>(w + L.rank),
+                            reinterpret_cast<int32_t*>(w + L.perm),
+                            reinterpret_cast<double*>(w + L.uscore),
+                            reinterpret_cast<int64_t*>(w + L.ucost),
+                            reinterpret_cast<uint8_t*>(w + L.flag)};
+    hipError_t e = nf4k::launch_select_ex(err, denom, cost, ge, group_end ? ngroups : nl,
+                                          budget_bytes, k_cap, rule, selected, k_out, scr, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 

@@ -30,10 +30,11 @@ __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileElems 
 
 // Fused blockwise quantisation (+ int8 double quantisation when dq) and, when
 // err_partial != nullptr, in-register dequantisation and the fp64 squared
-// error, written as kPartsPerTile partials per tile to err_partial.  ragged:
-// some layer's n is not a multiple of kTileElems (adds the tail launch).
+// error, written as kPartsPerTile partials per tile to err_partial; with
+// sq_partial != nullptr too, also the sum of x^2, laid out the same way.
+// ragged: some layer's n is not a multiple of kTileElems (adds the tail launch).
 hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, int dtype,
-                        bool dq, double* err_partial, hipStream_t s);
+                        bool dq, double* err_partial, double* sq_partial, hipStream_t s);
 // Per-layer fixed-order sum of the per-tile partials into err[nl].
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
                          hipStream_t s);
@@ -46,5 +47,18 @@ hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hip
 hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,
                          int kcap, uint8_t* selected, int32_t* k_out, int32_t* rank,
                          int32_t* perm, hipStream_t s);
+// Selection variants: unit = layer, or group of consecutive layers when
+// group_end (device, nu entries) is given; score = err (/ denom when given);
+// rule 0 = longest prefix within the budget, 1 = fill past what does not fit.
+struct SelectScratch {
+    int32_t* rank;    // [nu]
+    int32_t* perm;    // [nu]
+    double* uscore;   // [nu]
+    int64_t* ucost;   // [nu]
+    uint8_t* flag;    // [nu]
+};
+hipError_t launch_select_ex(const double* err, const double* denom, const int64_t* cost,
+                            const int32_t* group_end, int nu, int64_t budget, int kcap, int rule,
+                            uint8_t* selected, int32_t* k_out, SelectScratch w, hipStream_t s);
 
 }  // namespace nf4k

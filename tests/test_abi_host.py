@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(q.EXPORTS), set(names) ^ set(q.EXPORTS)
-    assert q.nf4_abi_version() == 1
+    assert q.nf4_abi_version() == 2
 
 
 def test_embedded_levels_and_thresholds_equal_the_oracles():
@@ -57,11 +57,13 @@ def test_workspace_sizes():
     f = q.fmt()
     ns = [16384 * 3 + 1, 100, 64]
     tiles = 4 + 1 + 1
-    # layer table (64 B per matrix) + 4 fp64 error partials per tile of 16384 weights
-    assert q.nf4_workspace_bytes(ns, f) == 256 + ((tiles * 4 * 8 + 255) // 256) * 256
+    # layer table (64 B per matrix) + 4 fp64 error partials and 4 fp64 sum-of-squares
+    # partials per tile of 16384 weights
+    assert q.nf4_workspace_bytes(ns, f) == 256 + 2 * (((tiles * 4 * 8 + 255) // 256) * 256)
     assert q.nf4_workspace_bytes([], f) == 0
     assert q.nf4_workspace_bytes([0], f) == 0
-    assert q.aqlora_workspace_bytes(280) == 2 * 1280
+    # rank, perm, staged group ends (int32), unit scores, unit costs (8 B), flags (1 B)
+    assert q.aqlora_workspace_bytes(280) == 3 * 1280 + 2 * 2304 + 512
     assert q.aqlora_workspace_bytes(0) == 0
     assert q.aqlora_workspace_bytes(65537) == 0
 
@@ -131,9 +133,11 @@ def test_misaligned_pointers(name):
 def test_workspace_checks(name):
     f = q.fmt()
     ns = [16384 * 5 + 3]
-    need = q.nf4_workspace_bytes(ns, f)
     tab_only = 256
-    small = (tab_only - 1) if name != "nf4_layer_error" else (need - 1)
+    tiles = (ns[0] + 16383) // 16384
+    err_only = tab_only + ((tiles * 4 * 8 + 255) // 256) * 256   # table + error partials
+    assert q.nf4_workspace_bytes(ns, f) == tab_only + 2 * (err_only - tab_only)
+    small = (tab_only - 1) if name != "nf4_layer_error" else (err_only - 1)
     assert _call(name, [_L(n=ns[0])], f, ws=None) == q.NF4_E_WORKSPACE
     assert _call(name, [_L(n=ns[0])], f, ws=FAKE + 64) == q.NF4_E_WORKSPACE
     assert _call(name, [_L(n=ns[0])], f, ws_bytes=small) == q.NF4_E_WORKSPACE
@@ -172,3 +176,57 @@ def test_hip_failure_surfaces_as_status():
     st = _call("nf4_quantize", [_L()], q.fmt())
     assert st == q.NF4_E_HIP
     assert q.lib().nf4_last_hip_error() != 0
+
+
+def test_layer_error_norm_arguments():
+    L = q.lib()
+    f = q.fmt()
+    ns = [16384 * 5 + 3]
+    arr = (q.nf4_layer * 1)(_L(n=ns[0]))
+    need = q.nf4_workspace_bytes(ns, f)
+    ok = dict(err=FAKE, sq=FAKE + 1024, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.nf4_layer_error_norm(arr, 1, f, a["err"], a["sq"], a["ws"], a["wsb"], None)
+    assert call(sq=None) == q.NF4_E_ARG
+    assert call(err=None) == q.NF4_E_ARG
+    assert call(sq=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(err=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(wsb=need - 1) == q.NF4_E_WORKSPACE      # needs both partial arrays
+    assert L.nf4_layer_error_norm(arr, 0, f, FAKE, FAKE, FAKE, need, None) == q.NF4_E_ARG
+    assert L.nf4_layer_error_norm(arr, 1, q.nf4_format(0, 32, 0), FAKE, FAKE, FAKE, need,
+                                  None) == q.NF4_E_UNSUPPORTED
+
+
+def test_select_variant_argument_errors():
+    L = q.lib()
+    nl = 10
+    ge_ok = np.array([3, 7, 10], np.int32)
+    ok = dict(err=FAKE, denom=None, cost=FAKE, nl=nl, ge=ge_ok, ng=3, budget=-1, kcap=-1,
+              rule=0, sel=FAKE, k=FAKE, ws=FAKE, wsb=q.aqlora_workspace_bytes(nl))
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        ge = a["ge"]
+        gp = None if ge is None else np.ascontiguousarray(ge, np.int32).ctypes.data
+        return L.aqlora_select(a["err"], a["denom"], a["cost"], a["nl"], gp, a["ng"],
+                               a["budget"], a["kcap"], a["rule"], a["sel"], a["k"], a["ws"],
+                               a["wsb"], None)
+    for fld in ("err", "cost", "sel", "k"):
+        assert call(**{fld: None}) == q.NF4_E_ARG
+    assert call(nl=0) == q.NF4_E_ARG
+    assert call(nl=65537, ge=None) == q.NF4_E_ARG
+    assert call(rule=2) == q.NF4_E_ARG
+    assert call(rule=-1) == q.NF4_E_ARG
+    assert call(ge=[3, 7, 9], ng=3) == q.NF4_E_ARG          # last != nl
+    assert call(ge=[3, 3, 10], ng=3) == q.NF4_E_ARG         # not strictly increasing
+    assert call(ge=[0, 5, 10], ng=3) == q.NF4_E_ARG         # empty first group
+    assert call(ge=[3, 7, 10], ng=0) == q.NF4_E_ARG
+    assert call(ge=np.arange(1, 12, dtype=np.int32), ng=11) == q.NF4_E_ARG   # ngroups > nl
+    assert call(err=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(denom=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(cost=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(k=FAKE + 2) == q.NF4_E_ALIGN
+    assert call(ws=None) == q.NF4_E_WORKSPACE
+    assert call(wsb=q.aqlora_workspace_bytes(nl) - 1) == q.NF4_E_WORKSPACE

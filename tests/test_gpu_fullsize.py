@@ -110,6 +110,36 @@ def test_full_stack(key):
         if key in PREDICTED_K and g in PREDICTED_K[key]:
             assert ref_k == PREDICTED_K[key][g], (g, ref_k)
 
+    # selection variants on the GPU's scores: relative error, transformer-block
+    # units, both budget rules (oracle rule on the same scores, bit-exact)
+    sq = torch.empty_like(err)
+    err3 = torch.empty_like(err)
+    q.nf4_layer_error_norm(ls, f, err3, sq, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(err3.view(torch.int64), err.view(torch.int64))
+    sqs = sq.cpu().numpy()
+    m = len(cfg.per_block)
+    ge = np.arange(m, nl + 1, m, dtype=np.int32)
+    sws = torch.empty(q.aqlora_workspace_bytes(nl), dtype=torch.uint8, device="cuda")
+    for g in cfg.budgets_gib:
+        for denom in (None, sq):
+            for groups in (None, ge):
+                for rule in (q.AQLORA_PREFIX, q.AQLORA_FILL):
+                    sel = torch.empty(nl, dtype=torch.uint8, device="cuda")
+                    k = torch.empty(1, dtype=torch.int32, device="cuda")
+                    q.aqlora_select(err, cost, int(g * (1 << 30)), cfg.kcap, sel, k, sws,
+                                    denom=denom, group_end=groups, rule=rule)
+                    ref_sel, ref_k = oracle.select(errs, costs, int(g * (1 << 30)), cfg.kcap,
+                                                   denom=None if denom is None else sqs,
+                                                   group_end=groups, rule=rule)
+                    torch.cuda.synchronize()
+                    assert k.item() == ref_k and np.array_equal(sel.cpu().numpy(), ref_sel), \
+                        (g, denom is None, groups is None, rule)
+    for i in range(nl):
+        x = ls.w_of(i).view(torch.bfloat16).double()
+        ref = float((x * x).sum().item())
+        assert abs(sqs[i] - ref) <= ERR_RTOL * ref, (cfg.layers[i][0], sqs[i], ref)
+
     # dequantise what is left in NF4 (the bench's launch), then the promoted rest
     g0 = cfg.budgets_gib[0]
     selected = selections[g0][0].cpu().numpy().astype(bool)
