@@ -185,6 +185,63 @@ def variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes, r
     return res
 
 
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def matmul_block(q, torch, ls, f, cfg, stream, m=4096, reps=10):
+    """The NF4 weight consumed by its matmul (fused dequantisation on the
+    matrix cores) on one FFN up-projection of the stack, m tokens, against
+    the library bf16 GEMM on the dequantised weight and the standalone
+    dequantisation (the dequantise-then-multiply pattern)."""
+    names = [nm for nm, _, _ in cfg.per_block]
+    li = names.index("up") if "up" in names else 0
+    _, rows, cols = cfg.per_block[li]
+    layer = ls.c_layers[li]
+    sub = ls.subset([li])
+    ws1 = torch.empty(q.nf4_workspace_bytes([rows * cols], f), dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    x = torch.randn(m, cols, dtype=torch.bfloat16, device="cuda", generator=gen)
+    gy = torch.randn(m, rows, dtype=torch.bfloat16, device="cuda", generator=gen)
+    yf = torch.empty(m, rows, dtype=torch.bfloat16, device="cuda")
+    yb = torch.empty(m, cols, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            e[2 * r].record(stream)
+            fn()
+            e[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[2 * r].elapsed_time(e[2 * r + 1]) for r in range(reps)) / reps
+
+    t_fwd = timed(lambda: q.nf4_matmul(layer, rows, cols, f, x.view(torch.int16), yf))
+    t_bwd = timed(lambda: q.nf4_matmul(layer, rows, cols, f, gy.view(torch.int16), yb,
+                                       backward=True))
+    t_deq = timed(lambda: q.nf4_dequantize(sub, f, ws1))
+    w = ls.out_of(li).view(torch.bfloat16).view(rows, cols)
+    wt = w.t().contiguous()
+    t_lib_f = timed(lambda: torch.matmul(x, wt))
+    t_lib_b = timed(lambda: torch.matmul(gy, w))
+    flops = 2.0 * m * rows * cols
+    tf = lambda t: round(flops / (t * 1e-3) / 1e12, 1)
+    res = {
+        "shape": {"m": m, "rows": rows, "cols": cols, "matrix": names[li]},
+        "fused_fwd_ms": round(t_fwd, 4), "fused_fwd_TFLOPs": tf(t_fwd),
+        "fused_bwd_ms": round(t_bwd, 4), "fused_bwd_TFLOPs": tf(t_bwd),
+        "library_bf16_fwd_ms": round(t_lib_f, 4), "library_bf16_fwd_TFLOPs": tf(t_lib_f),
+        "library_bf16_bwd_ms": round(t_lib_b, 4), "library_bf16_bwd_TFLOPs": tf(t_lib_b),
+        "dequant_ms": round(t_deq, 4),
+        "dequant_then_library_fwd_ms": round(t_deq + t_lib_f, 4),
+        "roofline": {"bound": "mfma", "kernel": "nf4_matmul forward",
+                     "achieved": tf(t_fwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tf(t_fwd) / MFMA_BF16_PEAK_TFS, 4)},
+    }
+    del x, gy, yf, yb, wt, ws1
+    return res
+
+
 def protocol_arms(launch, seconds: float, torch, stream):
     """Fixed-duration timing with a duplicated arm: the same launch is timed as
     arms A and A2 in alternating blocks of about 0.2 s until each has run for
@@ -375,6 +432,9 @@ def main():
     }
     if not args.no_variants:
         out["variants"] = variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes)
+        if cfg.dtype == q.NF4_BF16 and all(r % 128 == 0 and c % 128 == 0
+                                             for _, r, c in cfg.per_block):
+            out["matmul"] = matmul_block(q, torch, ls, f, cfg, stream)
     if args.protocol > 0:
         sub = subsets[keep]
         out["protocol"] = {

@@ -213,3 +213,16 @@ def select(err, cost, budget: int = -1, kcap: int = -1, denom=None, group_end=No
     K = lib().nf4o_select(_p(err), _p(d), _p(cost), nl, _p(g), 0 if g is None else g.size,
                           int(budget), int(kcap), int(rule), _p(sel))
     return sel, K
+
+
+def matmul(x_bits, rows: int, cols: int, codes, dtype: int = BF16, absmax=None, qabsmax=None,
+           scale2=None, backward: bool = False) -> np.ndarray:
+    """The matmul that consumes an NF4 weight, in fp64: W [rows x cols] is
+    dequantised by the oracle (the 16-bit values nf4o_dequantize defines),
+    then forward x[m x cols] @ W^T, backward x[m x rows] @ W.  x_bits: 16-bit
+    patterns of x.  The product is numpy's fp64 matmul of the exact values."""
+    w = from16(dequantize(codes, rows * cols, dtype, absmax, qabsmax, scale2), dtype)
+    w = w.astype(np.float64).reshape(rows, cols)
+    x = from16(np.ascontiguousarray(x_bits, np.uint16), dtype).astype(np.float64)
+    x = x.reshape(-1, rows if backward else cols)
+    return x @ w if backward else x @ w.T

@@ -76,6 +76,9 @@ EXPORTS = {
                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]),
+    "nf4_matmul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, nf4_format,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "nf4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32, nf4_format]),
     "aqlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
     "nf4_storage_bytes": (ctypes.c_int64, [ctypes.c_int64, nf4_format]),
@@ -194,6 +197,18 @@ def aqlora_select(err, cost, budget_bytes: int, k_cap: int, selected, k_out, ws,
                                int(rule), _ptr(selected), _ptr(k_out), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)),
            "aqlora_select")
+
+
+def nf4_matmul(layer, rows: int, cols: int, f: nf4_format, x, out, backward: bool = False,
+               stream=None) -> None:
+    """out = x @ W^T (forward) or x @ W (backward) with W in NF4 form.
+    layer: an nf4_layer struct (e.g. ls.c_layers[i]); x, out: device tensors
+    (out float32 or bfloat16)."""
+    import torch
+    m = int(x.shape[0]) if x.dim() > 1 else 1
+    out_fp32 = 1 if out.dtype == torch.float32 else 0
+    _check(lib().nf4_matmul(ctypes.byref(layer), int(rows), int(cols), f, int(bool(backward)),
+                            _ptr(x), m, _ptr(out), out_fp32, _stream(stream)), "nf4_matmul")
 
 
 # ---- host helpers ---------------------------------------------------------

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libnf4.so")
-SOURCES = ["k_codec.hip", "k_select.hip", "nf4_api.cpp"]
+SOURCES = ["k_codec.hip", "k_select.hip", "k_gemm.hip", "nf4_api.cpp"]
 ARCH = os.environ.get("NF4_OFFLOAD_ARCH", "gfx950")
 
 

@@ -1,0 +1,334 @@
+// k_gemm.hip -- NF4 dequantisation fused into the 16-bit matmul that consumes
+// the weight, on gfx950 matrix cores (MFMA).
+//
+// QLoRA keeps the frozen weight in 4 bits and dequantises it on the fly for
+// the forward and the backward pass ("QLoRA" paper summary page, How It
+// Works); AQLoRA names that per-step dequantisation as where quantised
+// fine-tuning loses its time (AQLoRA arXiv listing, English abstract).  Here
+// the weight tile is dequantised straight into LDS, in the value the codec
+// defines (y = RNE16(fl32(level[code] * dequantised absmax)), bitwise what
+// nf4_dequantize writes), and multiplied there: the 16-bit weight never goes
+// to HBM.
+//
+//   forward   out[m, n] = sum_k x[m, k] * W[n, k]      (x: m x cols, out: m x rows)
+//   backward  out[m, k] = sum_n x[m, n] * W[n, k]      (x: m x rows, out: m x cols)
+//
+// One kernel serves both: the first operand A is always row-major with the
+// reduction index contiguous (x, or the output gradient); the W tile is
+// stored in LDS with the reduction index contiguous too -- in W's own order
+// forward, transposed backward -- so the MFMA fragment reads are the same.
+//
+// Tiling: a 256-thread workgroup computes a 128 x 128 output tile in k-steps
+// of 64 (one quantisation block of a W row forward); waves in a 2 x 2 grid,
+// each 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.  The next step's A rows and W codes are loaded into registers
+// (raw: no wait) while the current step multiplies; after a barrier they are
+// dequantised into the single LDS buffer.  37 KB of LDS per workgroup lets 3
+// workgroups share a CU, which measured faster than double buffering at 2.
+// Products of two bf16 values are exact in fp32; only the fp32 accumulation
+// rounds.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nf4_format.h"
+#include "nf4_internal.h"
+
+namespace nf4k {
+namespace {
+
+#ifndef NF4_GEMM_STAGES
+#define NF4_GEMM_STAGES 1         // LDS buffers; one (two barriers per step) leaves room for 3 workgroups per CU
+#endif
+#ifndef NF4_GEMM_WM
+#define NF4_GEMM_WM 64            // output rows per wave
+#endif
+#ifndef NF4_GEMM_WN
+#define NF4_GEMM_WN 64            // output columns per wave
+#endif
+constexpr int kGThreads = 256;
+constexpr int kWM = NF4_GEMM_WM, kWN = NF4_GEMM_WN;
+constexpr int kTM = kWM / 32, kTN = kWN / 32;   // 32 x 32 MFMA tiles per wave
+constexpr int kBM = 2 * kWM;      // output rows (of x) per workgroup
+constexpr int kBN = 2 * kWN;      // output columns per workgroup
+constexpr int kBK = 64;           // reduction step
+constexpr int kAChunks = kBM / 32;   // 16-byte A chunks per thread and step
+constexpr int kWPass = kBN / 128;    // W passes per thread and step
+static_assert(kBN % 128 == 0 && kBM % 32 == 0, "tile shape");
+constexpr int kLdp = kBK + 8;     // LDS row pitch in 16-bit elements (144 B: conflict-free 16-B reads)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define GLOBAL __attribute__((address_space(1)))
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// Two fp32 values rounded to bf16 (nearest, ties to even), packed low first.
+__device__ __forceinline__ uint32_t pack_bf16(float y0, float y1)
+{
+    f2 in = {y0, y1};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(in, bf2));
+}
+
+struct GemmArgs {
+    const uint16_t* a;      // [M x kred] bf16 bits, row pitch lda
+    int64_t lda;
+    const uint8_t* codes;   // W codes, W row-major [rows x cols]
+    const int8_t* qabsmax;  // per 64-block (double quant) ...
+    const float* scale2;    // ... and per 256 blocks
+    const float* absmax;    // per 64-block (no double quant)
+    int64_t cols;           // W row length
+    void* out;              // [M x ncol], row pitch ldo
+    int64_t ldo;
+    int64_t M, kred, ncol;
+    int64_t ntn;            // output column tiles
+    int64_t tile0;          // first tile of this launch
+};
+
+// Raw constant of W block b as loaded: the int8 and its group scale with
+// double quant, else the fp32 absmax.  Kept raw until the dequantisation so
+// that the loads stay in flight while the previous step multiplies.
+struct RawConst {
+    int32_t q;
+    float s;
+};
+
+template <bool DQ>
+__device__ __forceinline__ RawConst load_const(const GemmArgs& g, int64_t b)
+{
+    if constexpr (DQ) return RawConst{((const GLOBAL int8_t*)g.qabsmax)[b], ((const GLOBAL float*)g.scale2)[b >> 8]};
+    else return RawConst{0, ((const GLOBAL float*)g.absmax)[b]};
+}
+
+// The dequantised constant (fl32 product with double quant).
+template <bool DQ>
+__device__ __forceinline__ float block_const(const RawConst& c)
+{
+    if constexpr (DQ) return (float)c.q * c.s;
+    else return c.s;
+}
+
+// Eight codes (one dword, element 2j in the low nibble of byte j) to eight
+// bf16 values, packed in four dwords.
+__device__ __forceinline__ u32x4 deq8(uint32_t c, float adq, const float* lv)
+{
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        r[j] = pack_bf16(lv[(c >> (8 * j)) & 15] * adq, lv[(c >> (8 * j + 4)) & 15] * adq);
+    return r;
+}
+
+// Per-step loads held in registers while the previous step multiplies.
+struct StepRegs {
+    u32x4 a[kAChunks];        // 16-byte chunks of A rows
+    uint32_t w[kWPass][4];    // codes: forward 4 dwords of one W row; backward 1 dword of 4 W rows
+    RawConst k[kWPass][4];    // forward: [p][0]; backward: one per W row
+};
+
+template <bool FWD, bool DQ>
+__device__ __forceinline__ void load_step(StepRegs& r, const GemmArgs& g, int64_t m0, int64_t c0,
+                                          int64_t k0)
+{
+    const int t = threadIdx.x;
+    // A: kBM rows x 64 elements; thread t: rows (t >> 3) + 32 i, 16-byte chunk t & 7.
+    // Rows past M load row M-1 instead: they only feed output rows that are
+    // not stored, and an unconditional load never waits for the one before.
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+        int64_t row = m0 + (t >> 3) + 32 * i;
+        row = row < g.M ? row : g.M - 1;
+        r.a[i] = *(const GLOBAL u32x4*)(g.a + row * g.lda + k0 + 8 * (t & 7));
+    }
+#pragma unroll
+    for (int p = 0; p < kWPass; ++p) {
+        if constexpr (FWD) {
+            // W rows c0 .. c0+kBN-1 (output columns), cols k0 .. k0+63: thread t takes
+            // 32 codes of row c0 + 128 p + (t >> 1), half t & 1; one block per row
+            const int64_t n = c0 + 128 * p + (t >> 1);
+            const int64_t e = n * g.cols + k0 + 32 * (t & 1);
+            const u32x4 c = *(const GLOBAL u32x4*)(g.codes + (e >> 1));
+            r.w[p][0] = c.x; r.w[p][1] = c.y; r.w[p][2] = c.z; r.w[p][3] = c.w;
+            r.k[p][0] = load_const<DQ>(g, e >> 6);
+        } else {
+            // W rows k0 .. k0+63 (the reduction), cols c0 .. c0+kBN-1 (output columns):
+            // thread t takes rows k0 + 4 (t & 15) + i, cols c0 + 128 p + 8 (t >> 4) .. + 8
+            // (16 consecutive lanes: 64 consecutive rows of one 8-column group, so
+            // that their transposed LDS writes form one contiguous 128-byte row)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t n = k0 + 4 * (t & 15) + i;
+                const int64_t e = n * g.cols + c0 + 128 * p + 8 * (t >> 4);
+                r.w[p][i] = *(const GLOBAL uint32_t*)(g.codes + (e >> 1));
+                r.k[p][i] = load_const<DQ>(g, e >> 6);
+            }
+        }
+    }
+}
+
+template <bool FWD, bool DQ>
+__device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint16_t* Ws,
+                                           const float* lv)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i)
+        *(u32x4*)(As + ((t >> 3) + 32 * i) * kLdp + 8 * (t & 7)) = r.a[i];
+#pragma unroll
+    for (int p = 0; p < kWPass; ++p) {
+        if constexpr (FWD) {
+            // W tile in W's order: Ws[n][k]
+            uint16_t* dst = Ws + (128 * p + (t >> 1)) * kLdp + 32 * (t & 1);
+            const float adq = block_const<DQ>(r.k[p][0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *(u32x4*)(dst + 8 * j) = deq8(r.w[p][j], adq, lv);
+        } else {
+            // transposed: Ws[k][n] with the reduction index n contiguous; this thread's
+            // four rows n0..n0+3 are consecutive, so each column gets one 8-byte write
+            u32x4 y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = deq8(r.w[p][i], block_const<DQ>(r.k[p][i]), lv);
+            const int n0 = 4 * (t & 15), cc = 128 * p + 8 * (t >> 4);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int j = c >> 1, hi = (c & 1) * 16;
+                const uint32_t v0 = ((y[0][j] >> hi) & 0xffffu) | (((y[1][j] >> hi) & 0xffffu) << 16);
+                const uint32_t v1 = ((y[2][j] >> hi) & 0xffffu) | (((y[3][j] >> hi) & 0xffffu) << 16);
+                *(u32x2*)(Ws + (cc + c) * kLdp + n0) = u32x2{v0, v1};
+            }
+        }
+    }
+}
+
+template <bool FWD, bool DQ, bool OUT_F32>
+__global__ __launch_bounds__(kGThreads) void k_nf4_matmul(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[NF4_GEMM_STAGES][kBM * kLdp];
+    __shared__ __attribute__((aligned(16))) uint16_t s_w[NF4_GEMM_STAGES][kBN * kLdp];
+    __shared__ float s_lv[16];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    if (t < 16) s_lv[t] = as_f(nf4fmt::kLevelBits[t]);
+
+    const int64_t tile = g.tile0 + blockIdx.x;
+    const int64_t m0 = (tile / g.ntn) * kBM;
+    const int64_t c0 = (tile % g.ntn) * kBN;
+    const int wm = wv >> 1, wn = wv & 1;   // this wave's kWM x kWN quarter
+    const int nsteps = (int)(g.kred / kBK);
+
+    f32x16 acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    StepRegs regs;
+    load_step<FWD, DQ>(regs, g, m0, c0, 0);
+    __syncthreads();   // level table
+    store_step<FWD, DQ>(regs, s_a[0], s_w[0], s_lv);
+    __syncthreads();
+
+    for (int s = 0; s < nsteps; ++s) {
+        const int cur = NF4_GEMM_STAGES == 2 ? (s & 1) : 0;
+        const bool more = s + 1 < nsteps;
+        if (more) load_step<FWD, DQ>(regs, g, m0, c0, (int64_t)(s + 1) * kBK);
+        const uint16_t* As = s_a[cur];
+        const uint16_t* Ws = s_w[cur];
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int kof = 16 * kk + 8 * (lane >> 5);
+            bf16x8 fa[kTM], fb[kTN];
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+                fa[i] = *(const bf16x8*)(As + (kWM * wm + 32 * i + (lane & 31)) * kLdp + kof);
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+                fb[j] = *(const bf16x8*)(Ws + (kWN * wn + 32 * j + (lane & 31)) * kLdp + kof);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (NF4_GEMM_STAGES == 1) __syncthreads();   // every wave done reading the one buffer
+        if (more) store_step<FWD, DQ>(regs, s_a[cur ^ (NF4_GEMM_STAGES - 1)],
+                                      s_w[cur ^ (NF4_GEMM_STAGES - 1)], s_lv);
+        __syncthreads();
+    }
+
+    // D layout of a 32 x 32 tile: lane l, value r -> row 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column l % 32
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + kWM * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int64_t col = c0 + kWN * wn + 32 * j + (lane & 31);
+                if (row < g.M) {
+                    if constexpr (OUT_F32)
+                        ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
+                    else
+                        ((GLOBAL uint16_t*)g.out)[row * g.ldo + col] =
+                            (uint16_t)pack_bf16(acc[i][j][r], 0.0f);
+                }
+            }
+}
+
+// One-shot launches of at most 2^32 / 256 - 1 workgroups each.
+constexpr int64_t kMaxGemmGrid = (int64_t(1) << 32) / kGThreads - 1;
+
+template <bool FWD, bool DQ, bool OUT_F32>
+hipError_t gemm_go(GemmArgs g, hipStream_t s)
+{
+    const int64_t ntiles = ((g.M + kBM - 1) / kBM) * g.ntn;
+    for (int64_t t0 = 0; t0 < ntiles; t0 += kMaxGemmGrid) {
+        const int64_t n = ntiles - t0 < kMaxGemmGrid ? ntiles - t0 : kMaxGemmGrid;
+        g.tile0 = t0;
+        hipLaunchKernelGGL((k_nf4_matmul<FWD, DQ, OUT_F32>), dim3((unsigned)n), dim3(kGThreads), 0, s, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_nf4_matmul(const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
+                             const float* absmax, int64_t rows, int64_t cols, bool forward,
+                             const void* x, int64_t m, void* out, bool out_f32, hipStream_t s)
+{
+    GemmArgs g;
+    g.a = static_cast<const uint16_t*>(x);
+    g.codes = codes;
+    g.qabsmax = qabsmax;
+    g.scale2 = scale2;
+    g.absmax = absmax;
+    g.cols = cols;
+    g.out = out;
+    g.M = m;
+    g.kred = forward ? cols : rows;
+    g.ncol = forward ? rows : cols;
+    g.lda = g.kred;
+    g.ldo = g.ncol;
+    g.ntn = g.ncol / kBN;
+    g.tile0 = 0;
+    const bool dq = qabsmax != nullptr;
+#define NF4_GEMM(F, D, O) return gemm_go<F, D, O>(g, s)
+    if (forward) {
+        if (dq) { if (out_f32) NF4_GEMM(true, true, true); else NF4_GEMM(true, true, false); }
+        else    { if (out_f32) NF4_GEMM(true, false, true); else NF4_GEMM(true, false, false); }
+    } else {
+        if (dq) { if (out_f32) NF4_GEMM(false, true, true); else NF4_GEMM(false, true, false); }
+        else    { if (out_f32) NF4_GEMM(false, false, true); else NF4_GEMM(false, false, false); }
+    }
+#undef NF4_GEMM
+}
+
+}  // namespace nf4k

@@ -44,6 +44,14 @@ hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtyp
 // Standalone double quantisation of absmax.
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s);
 // Budgeted top-K; rank/perm are int32[nl] workspace arrays.
+// NF4 weight dequantised into the matmul that consumes it (bf16 MFMA):
+// forward out[m x rows] = x[m x cols] * W^T, backward out[m x cols] =
+// x[m x rows] * W; W [rows x cols] given by its codes and constants
+// (qabsmax + scale2 when qabsmax != nullptr, else absmax).  rows and cols
+// multiples of 128; out fp32 or bf16.
+hipError_t launch_nf4_matmul(const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
+                             const float* absmax, int64_t rows, int64_t cols, bool forward,
+                             const void* x, int64_t m, void* out, bool out_f32, hipStream_t s);
 hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,
                          int kcap, uint8_t* selected, int32_t* k_out, int32_t* rank,
                          int32_t* perm, hipStream_t s);

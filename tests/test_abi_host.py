@@ -230,3 +230,34 @@ def test_select_variant_argument_errors():
     assert call(k=FAKE + 2) == q.NF4_E_ALIGN
     assert call(ws=None) == q.NF4_E_WORKSPACE
     assert call(wsb=q.aqlora_workspace_bytes(nl) - 1) == q.NF4_E_WORKSPACE
+
+
+def test_matmul_arguments():
+    L = q.lib()
+    f = q.fmt()
+    rows, cols = 256, 384
+
+    def call(rows=rows, cols=cols, n=None, codes=FAKE, qa=FAKE, s2=FAKE, absmax=None, fmt=f,
+             backward=0, x=FAKE, m=10, out=FAKE, out_fp32=1):
+        lay = q.nf4_layer(rows * cols if n is None else n, None, codes, absmax, qa, s2, None)
+        return L.nf4_matmul(ctypes.byref(lay), rows, cols, fmt, backward, x, m, out, out_fp32, None)
+    assert call(fmt=q.fmt(q.NF4_FP16, True)) == q.NF4_E_UNSUPPORTED
+    assert call(fmt=q.nf4_format(0, 32, 256)) == q.NF4_E_UNSUPPORTED
+    assert call(rows=200, n=200 * cols) == q.NF4_E_UNSUPPORTED
+    assert call(cols=100, n=rows * 100) == q.NF4_E_UNSUPPORTED
+    assert call(n=rows * cols - 1) == q.NF4_E_ARG
+    assert call(m=0) == q.NF4_E_ARG
+    assert call(m=1 << 31) == q.NF4_E_ARG
+    assert call(backward=2) == q.NF4_E_ARG
+    assert call(out_fp32=3) == q.NF4_E_ARG
+    assert call(x=None) == q.NF4_E_ARG
+    assert call(out=None) == q.NF4_E_ARG
+    assert call(codes=None) == q.NF4_E_ARG
+    assert call(qa=None) == q.NF4_E_ARG
+    assert call(s2=None) == q.NF4_E_ARG
+    assert call(fmt=q.fmt(dq=False), absmax=None) == q.NF4_E_ARG
+    assert call(codes=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(x=FAKE + 8) == q.NF4_E_ALIGN
+    assert call(out=FAKE + 8) == q.NF4_E_ALIGN
+    assert call(s2=FAKE + 2) == q.NF4_E_ALIGN
+    assert L.nf4_matmul(None, rows, cols, f, 0, FAKE, 10, FAKE, 1, None) == q.NF4_E_ARG

@@ -1,0 +1,128 @@
+"""GPU parity of the fused NF4 matmul (nf4_matmul) against the oracle.
+
+The weight's NF4 form is made by the oracle on the host and uploaded, so the
+test isolates the matmul.  Reference: the oracle's dequantised weight and an
+fp64 product.  Bound (fp32 accumulation of exact bf16 products over K terms):
+|out - ref| <= 2 K 2^-24 (|x| |W|^T) elementwise.  The bf16 output equals the
+round-to-nearest-even of the same kernel's fp32 output.  Ragged m (1, 77,
+300), several tile counts, double quant on and off, forward and backward;
+the 14B stack's FFN shape (13824 x 5120) at m = 4096 on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_lora_fine_nf4_amd as q
+import synth
+from conftest import print_case
+
+pytestmark = pytest.mark.gpu
+BF16 = q.NF4_BF16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    q.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+class DevWeight:
+    """A matrix's NF4 form (from the oracle) in device memory."""
+
+    def __init__(self, rows, cols, seed, dq, outliers=0.0):
+        w = synth.generate_raw(seed, rows * cols, dtype=BF16, outlier_frac=outliers)
+        codes, absmax = oracle.quantize(w, BF16)
+        self.consts = dict(absmax=absmax)
+        self.codes = torch.from_numpy(codes).cuda()
+        self.absmax = torch.from_numpy(absmax).cuda()
+        self.q = self.s2 = None
+        if dq:
+            qa, s2 = oracle.double_quant(absmax)
+            self.consts = dict(qabsmax=qa, scale2=s2)
+            self.q = torch.from_numpy(qa).cuda()
+            self.s2 = torch.from_numpy(s2).cuda()
+        self.np_codes = codes
+        self.rows, self.cols, self.dq = rows, cols, dq
+        ptr = lambda t: None if t is None else int(t.data_ptr())
+        self.layer = q.nf4_layer(rows * cols, None, ptr(self.codes),
+                                 None if dq else ptr(self.absmax), ptr(self.q), ptr(self.s2), None)
+
+    def dense(self):
+        y = oracle.dequantize(self.np_codes, self.rows * self.cols, BF16, **self.consts)
+        return oracle.from16(y, BF16).astype(np.float64).reshape(self.rows, self.cols)
+
+
+def _x(m, k, seed):
+    rng = np.random.default_rng(seed)
+    return oracle.to16_rne(rng.standard_normal(m * k).astype(np.float32), BF16).reshape(m, k)
+
+
+def _run(W, xb, backward, out_f32=True):
+    m = xb.shape[0]
+    ncol = W.cols if backward else W.rows
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    out = torch.full((m, ncol), float("nan"), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                     device="cuda")
+    q.nf4_matmul(W.layer, W.rows, W.cols, q.fmt(BF16, W.dq), x, out, backward=backward)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(out, xb, W, backward, rows_idx=None):
+    x = oracle.from16(xb, BF16).astype(np.float64).reshape(xb.shape)
+    if rows_idx is not None:
+        x = x[rows_idx]
+    Wd = W.dense()
+    ref = x @ Wd if backward else x @ Wd.T
+    mag = np.abs(x) @ np.abs(Wd) if backward else np.abs(x) @ np.abs(Wd).T
+    K = W.rows if backward else W.cols
+    got = out.double().cpu().numpy()
+    if rows_idx is not None:
+        got = got[rows_idx]
+    assert np.all(np.isfinite(got))
+    bound = 2.0 * K * 2.0 ** -24 * mag + 1e-30
+    excess = np.abs(got - ref) / bound
+    worst = float(excess.max())
+    assert worst <= 1.0, (worst, np.unravel_index(int(excess.argmax()), excess.shape))
+    return worst
+
+
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+@pytest.mark.parametrize("dq", [False, True], ids=["nodq", "dq"])
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("m", [1, 77, 128, 300])
+def test_matmul_matches_oracle(m, shape, dq, backward):
+    rows, cols = shape
+    print_case("nf4_matmul", m, rows, cols, "dq" if dq else "nodq", "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 7000 + rows + cols, dq, outliers=0.002)
+    xb = _x(m, rows if backward else cols, 11 * m + rows)
+    out = _run(W, xb, backward)
+    _check(out, xb, W, backward)
+    # bf16 output: RNE of the same fp32 sums
+    o16 = _run(W, xb, backward, out_f32=False)
+    assert torch.equal(o16, out.to(torch.bfloat16))
+
+
+def test_matmul_is_deterministic():
+    W = DevWeight(256, 256, 42, True)
+    xb = _x(300, 256, 43)
+    a = _run(W, xb, False)
+    b = _run(W, xb, False)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_matmul_fullsize_ffn_sampled(backward):
+    rows, cols, m = 13824, 5120, 4096
+    print_case("nf4_matmul full size", rows, cols, m, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 99, True, outliers=0.0005)
+    xb = _x(m, rows if backward else cols, 100)
+    out = _run(W, xb, backward)
+    rng = np.random.default_rng(5)
+    idx = np.sort(np.r_[0, m - 1, rng.integers(0, m, 6)])
+    worst = _check(out, xb, W, backward, rows_idx=idx)
+    print(f"[{'bwd' if backward else 'fwd'}] worst error / bound {worst:.3f}", flush=True)
