@@ -23,10 +23,12 @@
 // each 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation.  The next step's A rows and W codes are loaded into registers
 // (raw: no wait) while the current step multiplies; after a barrier they are
-// dequantised into the single LDS buffer.  37 KB of LDS per workgroup lets 3
+// dequantised into the single LDS buffer.  39 KB of LDS per workgroup lets 3
 // workgroups share a CU, which measured faster than double buffering at 2.
-// Products of two bf16 values are exact in fp32; only the fp32 accumulation
-// rounds.
+// Level lookups read a 256-entry table of level pairs (one 8-byte read per
+// code byte).  Tiles are handed out in groups of 4 row tiles, each XCD taking
+// a contiguous run of that order.  Products of two bf16 values are exact in
+// fp32; only the fp32 accumulation rounds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,6 +40,15 @@ namespace {
 
 #ifndef NF4_GEMM_STAGES
 #define NF4_GEMM_STAGES 1         // LDS buffers; one (two barriers per step) leaves room for 3 workgroups per CU
+#endif
+#ifndef NF4_GEMM_GROUP_M
+#define NF4_GEMM_GROUP_M 4        // output row tiles per group of the tile order (0: row-major order)
+#endif
+#ifndef NF4_GEMM_XCD
+#define NF4_GEMM_XCD 1            // give each XCD a contiguous run of the tile order
+#endif
+#ifndef NF4_GEMM_LUT2
+#define NF4_GEMM_LUT2 1           // copies of a 256-entry table of level pairs (0: 16-entry level table)
 #endif
 #ifndef NF4_GEMM_WM
 #define NF4_GEMM_WM 64            // output rows per wave
@@ -117,9 +128,19 @@ __device__ __forceinline__ float block_const(const RawConst& c)
 __device__ __forceinline__ u32x4 deq8(uint32_t c, float adq, const float* lv)
 {
     u32x4 r;
+#if NF4_GEMM_LUT2
+    // lv: 256 (level[b & 15], level[b >> 4]) pairs per copy, copy chosen by lane
+    const f2* lp = (const f2*)lv + 256 * ((threadIdx.x & 63) % NF4_GEMM_LUT2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f2 p = lp[(c >> (8 * j)) & 255];
+        r[j] = pack_bf16(p.x * adq, p.y * adq);
+    }
+#else
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         r[j] = pack_bf16(lv[(c >> (8 * j)) & 15] * adq, lv[(c >> (8 * j + 4)) & 15] * adq);
+#endif
     return r;
 }
 
@@ -204,18 +225,46 @@ __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint
     }
 }
 
+#ifndef NF4_GEMM_MIN_WG
+#define NF4_GEMM_MIN_WG 3         // workgroups per CU the register allocation must allow
+#endif
+
 template <bool FWD, bool DQ, bool OUT_F32>
-__global__ __launch_bounds__(kGThreads) void k_nf4_matmul(GemmArgs g)
+__global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t s_a[NF4_GEMM_STAGES][kBM * kLdp];
     __shared__ __attribute__((aligned(16))) uint16_t s_w[NF4_GEMM_STAGES][kBN * kLdp];
-    __shared__ float s_lv[16];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+#if NF4_GEMM_LUT2
+    __shared__ __attribute__((aligned(16))) float s_lv[2 * 256 * NF4_GEMM_LUT2];
+    for (int i = t; i < 256 * NF4_GEMM_LUT2; i += kGThreads) {
+        const int b = i & 255;
+        s_lv[2 * i] = as_f(nf4fmt::kLevelBits[b & 15]);
+        s_lv[2 * i + 1] = as_f(nf4fmt::kLevelBits[b >> 4]);
+    }
+#else
+    __shared__ float s_lv[16];
     if (t < 16) s_lv[t] = as_f(nf4fmt::kLevelBits[t]);
+#endif
 
-    const int64_t tile = g.tile0 + blockIdx.x;
-    const int64_t m0 = (tile / g.ntn) * kBM;
-    const int64_t c0 = (tile % g.ntn) * kBN;
+    int64_t tile = g.tile0 + blockIdx.x;
+    if (NF4_GEMM_XCD && (gridDim.x & 7) == 0)
+        tile = g.tile0 + (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    int64_t mt, nt;
+    if (NF4_GEMM_GROUP_M > 0) {
+        const int64_t per = (int64_t)NF4_GEMM_GROUP_M * g.ntn;
+        const int64_t first = (tile / per) * NF4_GEMM_GROUP_M;
+        const int64_t mtiles = (g.M + kBM - 1) / kBM;
+        const int64_t gsz = mtiles - first < NF4_GEMM_GROUP_M ? mtiles - first : NF4_GEMM_GROUP_M;
+        const int64_t in = tile % per;
+        mt = first + in % gsz;
+        nt = in / gsz;
+    } else {
+        mt = tile / g.ntn;
+        nt = tile % g.ntn;
+    }
+    const int64_t m0 = mt * kBM;
+    const int64_t c0 = nt * kBN;
     const int wm = wv >> 1, wn = wv & 1;   // this wave's kWM x kWN quarter
     const int nsteps = (int)(g.kred / kBK);
 
