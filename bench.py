@@ -65,6 +65,31 @@ def read_traffic(workload_key: str, kernel: str):
     return float(v) if v else None
 
 
+def cpu_pass(cfg, n_total: int, blocks: int = 1):
+    """The multi-threaded host-CPU scoring pass (libnf4cpu.so, not the oracle)
+    on the first transformer block(s) of the stack, all host threads and one,
+    with the full-stack time it implies (the pass streams, so its rate does
+    not depend on the size)."""
+    import quantized_lora_fine_nf4_amd as q
+    from quantized_lora_fine_nf4_amd import cpu
+    import synth
+    f = q.fmt(cfg.dtype, cfg.dq)
+    m = len(cfg.per_block)
+    idx = list(range(min(cfg.n_layers, blocks * m)))
+    ws = [synth.generate(cfg, i) for i in idx]
+    n = sum(w.size for w in ws)
+    res = {"sample": f"first {len(idx)} matrices ({n} weights) of the stack", "weights": n}
+    for name, th in (("all_threads", 0), ("one_thread", 1)):
+        cpu.layer_error(ws, f, threads=th, with_absmax=not cfg.dq)   # warm (first touch)
+        t0 = time.perf_counter()
+        cpu.layer_error(ws, f, threads=th, with_absmax=not cfg.dq)
+        dt = time.perf_counter() - t0
+        res[name] = {"GBps": round(2.0 * n / dt / 1e9, 3), "s": round(dt, 3),
+                     "threads": cpu.max_threads() if th == 0 else 1,
+                     "full_stack_s": round(dt * n_total / n, 2)}
+    return res
+
+
 def cpu_baseline(cfg, seconds: float, n_deq: int, n_total: int):
     """The oracle (single-threaded C), untuned, on a bounded sample of the same
     workload: slices of 64 double-quant groups from successive matrices."""
@@ -451,6 +476,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, n_deq, n_total)
+        log("timing the multi-threaded CPU pass")
+        out["cpu_pass"] = cpu_pass(cfg, n_total)
     print(json.dumps(out), flush=True)
 
 

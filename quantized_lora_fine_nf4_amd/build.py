@@ -14,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libnf4.so")
+CPU_LIB_PATH = os.path.join(PKG, "libnf4cpu.so")
+CPU_SOURCES = [os.path.join("cpu", "nf4_cpu.cpp")]
 SOURCES = ["k_codec.hip", "k_select.hip", "k_gemm.hip", "nf4_api.cpp"]
 ARCH = os.environ.get("NF4_OFFLOAD_ARCH", "gfx950")
 
@@ -25,6 +27,26 @@ def command(out: str = LIB_PATH) -> list:
             "-Wall", "-Wno-unused-command-line-argument",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             "-o", out, *[os.path.join(CSRC, s) for s in SOURCES]]
+
+
+def cpu_command(out: str = CPU_LIB_PATH) -> list:
+    """The host-CPU pass (OpenMP, portable AVX2 target, no FMA contraction)."""
+    return ["g++", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", "-shared", "-fopenmp",
+            "-ffp-contract=off", "-fno-fast-math", "-Wall",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            "-o", out, *[os.path.join(PKG, s) for s in CPU_SOURCES]]
+
+
+def build_cpu(verbose: bool = False) -> str:
+    tmp = CPU_LIB_PATH + ".tmp"
+    cmd = cpu_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed ({r.returncode}):\n{r.stderr}")
+    os.replace(tmp, CPU_LIB_PATH)
+    return CPU_LIB_PATH
 
 
 def build(verbose: bool = False) -> str:
@@ -46,3 +68,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_cpu(verbose=True))
