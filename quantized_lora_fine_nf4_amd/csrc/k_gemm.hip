@@ -216,9 +216,12 @@ __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint
             const int n0 = 4 * (t & 15), cc = 128 * p + 8 * (t >> 4);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const int j = c >> 1, hi = (c & 1) * 16;
-                const uint32_t v0 = ((y[0][j] >> hi) & 0xffffu) | (((y[1][j] >> hi) & 0xffffu) << 16);
-                const uint32_t v1 = ((y[2][j] >> hi) & 0xffffu) | (((y[3][j] >> hi) & 0xffffu) << 16);
+                // the 16-bit value of column c from rows (0, 1) and (2, 3): one byte
+                // permute each (low halves: bytes 1:0 of each source, high: 3:2)
+                const int j = c >> 1;
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t v0 = __builtin_amdgcn_perm(y[1][j], y[0][j], sel);
+                const uint32_t v1 = __builtin_amdgcn_perm(y[3][j], y[2][j], sel);
                 *(u32x2*)(Ws + (cc + c) * kLdp + n0) = u32x2{v0, v1};
             }
         }
