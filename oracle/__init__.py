@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
             "nf4o_promote_cost": (i64, [i64, i32]),
             "nf4o_select_topk": (i32, [P, P, i32, i64, i32, P]),
             "nf4o_sumsq": (ctypes.c_double, [P, i64, i32]),
+            "nf4o_e4m3_decode": (ctypes.c_float, [ctypes.c_uint8]),
+            "nf4o_e4m3_encode": (ctypes.c_uint8, [ctypes.c_float]),
+            "nf4o_storage_bytes_ex": (i64, [i64, i32, i32]),
+            "nf4o_layer_error_ex": (ctypes.c_double, [P, i64, i32, i32, i32, P, P, P, P, P, P]),
             "nf4o_select": (i32, [P, P, P, i32, P, i32, i64, i32, i32, P]),
         }
         for name, (res, args) in sigs.items():
@@ -226,3 +230,35 @@ def matmul(x_bits, rows: int, cols: int, codes, dtype: int = BF16, absmax=None, 
     x = from16(np.ascontiguousarray(x_bits, np.uint16), dtype).astype(np.float64)
     x = x.reshape(-1, rows if backward else cols)
     return x @ w if backward else x @ w.T
+
+
+KIND_NONE, KIND_INT8, KIND_INT8_MEAN, KIND_FP8_MEAN = 0, 1, 2, 3
+
+
+def e4m3_decode(b: int) -> float:
+    return float(lib().nf4o_e4m3_decode(int(b)))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().nf4o_e4m3_encode(float(v)))
+
+
+def storage_bytes_ex(n: int, block: int, kind: int) -> int:
+    return int(lib().nf4o_storage_bytes_ex(int(n), int(block), int(kind)))
+
+
+def layer_error_ex(w: np.ndarray, dtype: int, block: int, kind: int) -> dict:
+    """Variant codec pass for one matrix -> dict(err, codes, absmax, q, scale2, mean, y)."""
+    w = np.ascontiguousarray(w, np.uint16).ravel()
+    n = w.size
+    nb = (n + block - 1) // block
+    ng = (nb + DQ_GROUP - 1) // DQ_GROUP
+    codes = np.empty((n + 1) // 2, np.uint8)
+    absmax = np.empty(nb, np.float32)
+    qv = np.zeros(nb, np.uint8)
+    s2 = np.zeros(ng, np.float32)
+    mean = np.zeros(1, np.float32)
+    y = np.empty(n, np.uint16)
+    err = lib().nf4o_layer_error_ex(_p(w), n, dtype, block, kind, _p(codes), _p(absmax), _p(qv),
+                                    _p(s2), _p(mean), _p(y))
+    return dict(err=err, codes=codes, absmax=absmax, q=qv, scale2=s2, mean=float(mean[0]), y=y)

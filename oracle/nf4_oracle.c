@@ -462,3 +462,137 @@ int nf4o_select(const double* err, const double* denom, const int64_t* cost, int
     free(take);
     return K;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Codec variants: block size and the kind of second-level quantisation.      */
+/* ------------------------------------------------------------------------- */
+/* [QLoRA page, How It Works, Double Quantization item] and [QLoRA explained,
+ * Double Quantization] say only that the constants are quantised again.
+ * Readings of the variants:
+ *   block: 32, 64, 128 or 256 consecutive weights share one absmax (the
+ *     encode rule is unchanged);
+ *   kind 0: no second level (fp32 absmax);
+ *   kind 1: int8, symmetric, per group of 256 blocks (the main reading);
+ *   kind 2: int8 of the absmax minus the matrix's mean absmax mu, per group:
+ *     c = fl32(a - mu), G = max |c|, s2 = fl32(G/127), q = clamp(rint(fl32(c/s2)),
+ *     -127, 127), a' = fl32(fl32(q * s2) + mu);
+ *   kind 3: as kind 2 with an 8-bit float (E4M3: 4 exponent bits, bias 7,
+ *     3 mantissa bits, largest 448, no infinities) in place of the int8:
+ *     s2 = fl32(G/448), q = E4M3 nearest (ties to even) of fl32(c/s2).
+ *   mu = fl32(S / nb), S the fp64 sum, in group order, of each group's fp64
+ *     sum of its absmax values in block order.
+ * Codes always use the exact absmax; dequantisation and the error use a'. */
+
+/* E4M3 byte -> value (the encodings with exponent 15 and mantissa 7 are NaN
+ * and never produced here). */
+float nf4o_e4m3_decode(uint8_t b)
+{
+    const int e = (b >> 3) & 15, m = b & 7;
+    float v = (e == 0) ? (float)m * 0x1p-9f : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return (b & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3 value of v (|v| <= 448), ties to the even encoding: a plain
+ * search over the 127 finite magnitudes; a negative value that rounds to zero
+ * gives -0. */
+uint8_t nf4o_e4m3_encode(float v)
+{
+    const float a = fabsf(v);
+    assert(a <= 448.0f);
+    int best = 0;
+    double bd = fabs((double)a - (double)nf4o_e4m3_decode(0));
+    for (int c = 1; c <= 0x7e; ++c) {
+        const double d = fabs((double)a - (double)nf4o_e4m3_decode((uint8_t)c));
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) { best = c; bd = d; }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));   /* the sign is kept, as IEEE rounding does */
+}
+
+int64_t nf4o_storage_bytes_ex(int64_t n, int block, int kind)
+{
+    const int64_t nb = (n + block - 1) / block;
+    const int64_t ng = (nb + NF4O_DQ_GROUP - 1) / NF4O_DQ_GROUP;
+    return (n + 1) / 2 + (kind == 0 ? 4 * nb : nb + 4 * ng + (kind >= 2 ? 4 : 0));
+}
+
+double nf4o_layer_error_ex(const uint16_t* w, int64_t n, int dtype, int block, int kind,
+                           uint8_t* codes, float* absmax, uint8_t* q, float* scale2,
+                           float* mean, uint16_t* y)
+{
+    const int64_t nb = (n + block - 1) / block;
+    const int64_t ng = (nb + NF4O_DQ_GROUP - 1) / NF4O_DQ_GROUP;
+    /* blockwise absmax and codes, exactly as nf4o_quantize with another block */
+    memset(codes, 0, (size_t)((n + 1) / 2));
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t lo = b * block, hi = (lo + block < n) ? lo + block : n;
+        float a = 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            const float ax = fabsf(nf4o_from16(w[i], dtype));
+            if (ax > a) a = ax;
+        }
+        absmax[b] = a;
+        float scale = 1.0f, r = 0.0f;
+        if (a > 0.0f) {
+            if (a < 0x1p-126f) scale = 0x1p64f;
+            r = 1.0f / (a * scale);
+        }
+        for (int64_t i = lo; i < hi; ++i) {
+            const int c = (a == 0.0f) ? 7 : nf4o_encode((nf4o_from16(w[i], dtype) * scale) * r);
+            codes[i >> 1] |= (uint8_t)(c << ((i & 1) * 4));
+        }
+    }
+    /* the dequantised constants */
+    float* ad = (float*)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1));
+    float mu = 0.0f;
+    if (kind >= 2) {
+        double S = 0.0;
+        for (int64_t g = 0; g < ng; ++g) {
+            double sg = 0.0;
+            for (int64_t b = g * NF4O_DQ_GROUP; b < nb && b < (g + 1) * NF4O_DQ_GROUP; ++b)
+                sg += (double)absmax[b];
+            S += sg;
+        }
+        mu = (float)(S / (double)nb);
+    }
+    if (mean) *mean = mu;
+    for (int64_t g = 0; g < ng; ++g) {
+        const int64_t lo = g * NF4O_DQ_GROUP, hi = (lo + NF4O_DQ_GROUP < nb) ? lo + NF4O_DQ_GROUP : nb;
+        if (kind == 0) {
+            for (int64_t b = lo; b < hi; ++b) ad[b] = absmax[b];
+            continue;
+        }
+        float G = 0.0f;
+        for (int64_t b = lo; b < hi; ++b) {
+            const float c = kind == 1 ? absmax[b] : absmax[b] - mu;
+            if (fabsf(c) > G) G = fabsf(c);
+        }
+        const float s2 = (G > 0.0f) ? G / (kind == 3 ? 448.0f : 127.0f) : 0.0f;
+        scale2[g] = s2;
+        for (int64_t b = lo; b < hi; ++b) {
+            const float c = kind == 1 ? absmax[b] : absmax[b] - mu;
+            if (kind == 3) {
+                float v = (s2 > 0.0f) ? c / s2 : 0.0f;
+                if (v > 448.0f) v = 448.0f;
+                if (v < -448.0f) v = -448.0f;
+                q[b] = nf4o_e4m3_encode(v);
+                ad[b] = nf4o_e4m3_decode(q[b]) * s2 + mu;
+            } else {
+                float qf = (s2 > 0.0f) ? rintf(c / s2) : 0.0f;
+                if (qf > 127.0f) qf = 127.0f;
+                if (qf < -127.0f) qf = -127.0f;
+                q[b] = (uint8_t)(int8_t)qf;
+                ad[b] = (float)(int8_t)q[b] * s2;
+                if (kind == 2) ad[b] = ad[b] + mu;
+            }
+        }
+    }
+    /* dequantise and score */
+    float v[16];
+    nf4o_levels(v);
+    for (int64_t i = 0; i < n; ++i) {
+        const int c = (codes[i >> 1] >> ((i & 1) * 4)) & 15;
+        y[i] = nf4o_to16_rne(v[c] * ad[i / block], dtype);
+    }
+    free(ad);
+    return nf4o_sse(w, y, n, dtype);
+}

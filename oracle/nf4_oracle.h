@@ -87,6 +87,19 @@ int      nf4o_select_topk(const double* err, const int64_t* cost, int nl,
  * group's last layer), rule 0 = stop at the first unit that does not fit,
  * rule 1 = skip it and keep filling.  Returns the number of units taken. */
 double   nf4o_sumsq(const uint16_t* w, int64_t n, int dtype);
+
+/* Codec variants: block size 32/64/128/256 and the second-level kind (0 none,
+ * 1 int8 symmetric, 2 int8 with the matrix's mean absmax subtracted, 3 E4M3
+ * 8-bit float with the mean subtracted), groups of 256 blocks.  q holds the
+ * int8 or E4M3 byte per block; mean (may be NULL) receives mu (0 for kinds
+ * 0 and 1).  Returns the reconstruction error; y receives the dequantised
+ * values. */
+float    nf4o_e4m3_decode(uint8_t b);
+uint8_t  nf4o_e4m3_encode(float v);
+int64_t  nf4o_storage_bytes_ex(int64_t n, int block, int kind);
+double   nf4o_layer_error_ex(const uint16_t* w, int64_t n, int dtype, int block, int kind,
+                             uint8_t* codes, float* absmax, uint8_t* q, float* scale2,
+                             float* mean, uint16_t* y);
 int      nf4o_select(const double* err, const double* denom, const int64_t* cost, int nl,
                      const int32_t* group_end, int ngroups, int64_t budget, int kcap,
                      int rule, uint8_t* selected);
