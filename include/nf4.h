@@ -85,6 +85,20 @@ typedef enum {
 
 typedef enum { NF4_BF16 = 0, NF4_FP16 = 1 } nf4_dtype;
 
+/* Codec variants: kind of the second-level quantisation of the constants. */
+typedef enum {
+    NF4_DQ_NONE = 0,       /* fp32 absmax per block                                       */
+    NF4_DQ_INT8 = 1,       /* int8 per block + fp32 scale per 256 blocks, symmetric        */
+    NF4_DQ_INT8_MEAN = 2,  /* as INT8, of the absmax minus the matrix's mean absmax        */
+    NF4_DQ_E4M3_MEAN = 3   /* 8-bit float E4M3 of the absmax minus the mean, fp32 scale    */
+} nf4_dq_kind;
+
+typedef struct {
+    int32_t dtype;      /* nf4_dtype                                   */
+    int32_t blocksize;  /* 32, 64, 128 or 256                          */
+    int32_t dq_kind;    /* nf4_dq_kind; groups of 256 blocks           */
+} nf4_variant;
+
 /* Budget rules of aqlora_select. */
 typedef enum {
     AQLORA_PREFIX = 0,  /* take units in rank order, stop at the first that does not fit */
@@ -189,6 +203,36 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
                          uint8_t* selected, int32_t* k_out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* Codec variants ("QLoRA" paper summary page, How It Works, Double
+ * Quantization item; "QLoRA Explained", Double Quantization: the constants
+ * are quantised again, without saying how).  Block size 32/64/128/256 and:
+ *   NF4_DQ_NONE      a' = a;
+ *   NF4_DQ_INT8      s2 = fl32(G/127) per 256 blocks (G their largest absmax),
+ *                    q = clamp(rint(fl32(a/s2))), a' = fl32(q s2);
+ *   NF4_DQ_INT8_MEAN c = fl32(a - mu), s2 = fl32(max|c|/127), q as above of
+ *                    fl32(c/s2), a' = fl32(fl32(q s2) + mu);
+ *   NF4_DQ_E4M3_MEAN as INT8_MEAN with s2 = fl32(max|c|/448) and q the nearest
+ *                    E4M3 value (ties to even, sign kept) of fl32(c/s2);
+ *   mu = fl32(S/nb), S the fp64 sum in group order of each group's fp64 sum of
+ *   its absmax values in block order.
+ * Codes use the exact absmax (the encode rule of the main codec with the block
+ * size changed); y = RNE16(fl32(level[code] a')); err = sum (x - y)^2 (fp64).
+ * layers: w (read, 16-byte aligned), codes (4-byte aligned), absmax (written:
+ * [ceil(n/block)] fp32), and for kinds 1-3 qabsmax (one byte per block: the
+ * int8, or the E4M3 encoding) and scale2 ([ceil(nb/256)] fp32).  mean: device
+ * fp32 [nl], written for kinds 2-3 (may be NULL otherwise).  err: device fp64
+ * [nl].  ws: nf4_workspace_bytes_variant.  The main codec (nf4_layer_error)
+ * is the fused fast path; this one takes three launches (absmax; mean;
+ * second level + encode + dequantise + error). */
+nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
+                                   float* mean, double* err, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Dequantisation of a variant's codes: reads codes, absmax (kind 0) or
+ * qabsmax + scale2 (+ mean for kinds 2-3); writes out (16-byte aligned). */
+nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
+                                  const float* mean, void* ws, size_t ws_bytes, void* stream);
+
 /* NF4 dequantisation fused into the 16-bit matmul that consumes the weight,
  * on the matrix cores.  QLoRA dequantises the 4-bit weight on the fly for the
  * forward and the backward pass ("QLoRA" paper summary page, How It Works);
@@ -219,6 +263,10 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
 size_t      nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format fmt);
 /* Workspace for aqlora_select_topk and aqlora_select; 0 on bad input. */
 size_t      aqlora_workspace_bytes(int32_t nl);
+/* Workspace for the variant calls (table + two fp64 per group); 0 on bad input. */
+size_t      nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_variant v);
+/* ceil(n/2) + (kind 0 ? 4 nb : nb + 4 ng) + (kinds 2-3 ? 4 : 0); -1 on bad input. */
+int64_t     nf4_storage_bytes_variant(int64_t n, nf4_variant v);
 /* ceil(n/2) + (dq_group ? nb + 4*ng : 4*nb); -1 on bad input. */
 int64_t     nf4_storage_bytes(int64_t n, nf4_format fmt);
 /* 2n - nf4_storage_bytes(n, fmt): extra bytes of keeping the matrix 16-bit. */

@@ -47,6 +47,14 @@ class nf4_format(ctypes.Structure):
                 ("dq_group", ctypes.c_int32)]
 
 
+class nf4_variant(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("blocksize", ctypes.c_int32),
+                ("dq_kind", ctypes.c_int32)]
+
+
+NF4_DQ_NONE, NF4_DQ_INT8, NF4_DQ_INT8_MEAN, NF4_DQ_E4M3_MEAN = range(4)
+
+
 class nf4_layer(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("w", ctypes.c_void_p), ("codes", ctypes.c_void_p),
                 ("absmax", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p),
@@ -80,6 +88,15 @@ EXPORTS = {
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "nf4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32, nf4_format]),
+    "nf4_layer_error_variant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_variant,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_size_t, ctypes.c_void_p]),
+    "nf4_dequantize_variant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_variant,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p]),
+    "nf4_workspace_bytes_variant": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32,
+                                                      nf4_variant]),
+    "nf4_storage_bytes_variant": (ctypes.c_int64, [ctypes.c_int64, nf4_variant]),
     "aqlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
     "nf4_storage_bytes": (ctypes.c_int64, [ctypes.c_int64, nf4_format]),
     "aqlora_promote_cost": (ctypes.c_int64, [ctypes.c_int64, nf4_format]),
@@ -211,6 +228,33 @@ def nf4_matmul(layer, rows: int, cols: int, f: nf4_format, x, out, backward: boo
                             _ptr(x), m, _ptr(out), out_fp32, _stream(stream)), "nf4_matmul")
 
 
+def variant(dtype: int = NF4_BF16, block: int = BLOCK, kind: int = NF4_DQ_INT8) -> nf4_variant:
+    return nf4_variant(int(dtype), int(block), int(kind))
+
+
+def nf4_layer_error_variant(layers, v: nf4_variant, err, ws, mean=None, stream=None) -> None:
+    arr, nl = _layers_arg(layers)
+    _check(lib().nf4_layer_error_variant(arr, nl, v, _ptr(mean), _ptr(err), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)),
+           "nf4_layer_error_variant")
+
+
+def nf4_dequantize_variant(layers, v: nf4_variant, ws, mean=None, stream=None) -> None:
+    arr, nl = _layers_arg(layers)
+    _check(lib().nf4_dequantize_variant(arr, nl, v, _ptr(mean), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)),
+           "nf4_dequantize_variant")
+
+
+def nf4_workspace_bytes_variant(ns, v: nf4_variant) -> int:
+    a = np.ascontiguousarray(ns, np.int64)
+    return int(lib().nf4_workspace_bytes_variant(a.ctypes.data if a.size else None, a.size, v))
+
+
+def nf4_storage_bytes_variant(n: int, v: nf4_variant) -> int:
+    return int(lib().nf4_storage_bytes_variant(int(n), v))
+
+
 # ---- host helpers ---------------------------------------------------------
 
 def nf4_workspace_bytes(ns, f: nf4_format) -> int:
@@ -263,12 +307,13 @@ class LayerSet:
     """
 
     def __init__(self, ns, f: nf4_format, device="cuda", with_out: bool = True,
-                 with_absmax: bool = True, w=None):
+                 with_absmax: bool = True, w=None, block: int = BLOCK):
         import torch
         self.ns = [int(n) for n in ns]
         self.fmt = f
         dq = f.dq_group != 0
-        nb = [(n + BLOCK - 1) // BLOCK for n in self.ns]
+        self.block = int(block)
+        nb = [(n + self.block - 1) // self.block for n in self.ns]
         ng = [(b + DQ_GROUP - 1) // DQ_GROUP for b in nb]
 
         def offsets(sizes, align):
@@ -321,15 +366,15 @@ class LayerSet:
         return self.codes[self.c_off[i]: self.c_off[i] + (self.ns[i] + 1) // 2]
 
     def absmax_of(self, i):
-        nb = (self.ns[i] + BLOCK - 1) // BLOCK
+        nb = (self.ns[i] + self.block - 1) // self.block
         return self.absmax[self.a_off[i]: self.a_off[i] + nb]
 
     def qabsmax_of(self, i):
-        nb = (self.ns[i] + BLOCK - 1) // BLOCK
+        nb = (self.ns[i] + self.block - 1) // self.block
         return self.qabsmax[self.a_off[i]: self.a_off[i] + nb]
 
     def scale2_of(self, i):
-        ng = ((self.ns[i] + BLOCK - 1) // BLOCK + DQ_GROUP - 1) // DQ_GROUP
+        ng = ((self.ns[i] + self.block - 1) // self.block + DQ_GROUP - 1) // DQ_GROUP
         return self.scale2[self.s_off[i]: self.s_off[i] + ng]
 
 

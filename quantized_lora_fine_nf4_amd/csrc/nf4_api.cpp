@@ -106,6 +106,40 @@ nf4_status stage_table(const nf4_layer* L, int32_t nl, void* ws, hipStream_t s)
     return NF4_OK;
 }
 
+// Table for the codec variants: tile_end counts groups of 256 blocks of the
+// variant's block size.
+nf4_status stage_table_variant(const nf4_layer* L, int32_t nl, int block, void* ws, hipStream_t s)
+{
+    std::vector<LayerDesc> tab(static_cast<size_t>(nl));
+    int64_t run = 0;
+    for (int32_t i = 0; i < nl; ++i) {
+        const int64_t nb = (L[i].n + block - 1) / block;
+        run += (nb + nf4fmt::kGroup - 1) / nf4fmt::kGroup;
+        tab[i] = LayerDesc{L[i].w, L[i].codes, L[i].absmax, L[i].qabsmax, L[i].scale2, L[i].out,
+                           L[i].n, run};
+    }
+    hipError_t e = hipMemcpyAsync(ws, tab.data(), sizeof(LayerDesc) * size_t(nl),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return NF4_OK;
+}
+
+nf4_status check_variant(const nf4_variant& v)
+{
+    if (v.blocksize != 32 && v.blocksize != 64 && v.blocksize != 128 && v.blocksize != 256)
+        return NF4_E_UNSUPPORTED;
+    if (v.dq_kind < NF4_DQ_NONE || v.dq_kind > NF4_DQ_E4M3_MEAN) return NF4_E_UNSUPPORTED;
+    if (v.dtype != NF4_BF16 && v.dtype != NF4_FP16) return NF4_E_UNSUPPORTED;
+    return NF4_OK;
+}
+
+int64_t variant_groups(const nf4_layer* L, int32_t nl, int block)
+{
+    int64_t g = 0;
+    for (int32_t i = 0; i < nl; ++i) g += ((L[i].n + block - 1) / block + nf4fmt::kGroup - 1) / nf4fmt::kGroup;
+    return g;
+}
+
 // The fused pass; with sumsq also the per-layer sum of x^2 (partials for it
 // follow the error partials in the workspace).
 nf4_status layer_error_impl(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
@@ -363,6 +397,74 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
                                            dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax,
                                            rows, cols, backward == 0, x, m, out, out_fp32 == 1,
                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+size_t nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_variant v)
+{
+    if (!n_per_layer || nl <= 0 || nl > kMaxLayers || check_variant(v) != NF4_OK) return 0;
+    int64_t g = 0;
+    for (int32_t i = 0; i < nl; ++i) {
+        if (n_per_layer[i] <= 0 || n_per_layer[i] >= kMaxN) return 0;
+        g += ((n_per_layer[i] + v.blocksize - 1) / v.blocksize + nf4fmt::kGroup - 1) / nf4fmt::kGroup;
+    }
+    return table_bytes(nl) + 2 * align256(size_t(g) * sizeof(double));
+}
+
+int64_t nf4_storage_bytes_variant(int64_t n, nf4_variant v)
+{
+    if (n <= 0 || n >= kMaxN || check_variant(v) != NF4_OK) return -1;
+    const int64_t nb = (n + v.blocksize - 1) / v.blocksize;
+    const int64_t ng = (nb + nf4fmt::kGroup - 1) / nf4fmt::kGroup;
+    return (n + 1) / 2 + (v.dq_kind == NF4_DQ_NONE ? 4 * nb : nb + 4 * ng) +
+           (v.dq_kind >= NF4_DQ_INT8_MEAN ? 4 : 0);
+}
+
+nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
+                                   float* mean, double* err, void* ws, size_t ws_bytes,
+                                   void* stream)
+{
+    nf4_status st = check_variant(v);
+    if (st != NF4_OK) return st;
+    if (!err) return NF4_E_ARG;
+    const bool second = v.dq_kind != NF4_DQ_NONE, with_mean = v.dq_kind >= NF4_DQ_INT8_MEAN;
+    if (with_mean && !mean) return NF4_E_ARG;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl, NEED_W | NEED_CODES | NEED_ABSMAX | (second ? NEED_Q | NEED_S2 : 0u),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if (!aligned(err, 8) || (with_mean && !aligned(mean, 4))) return NF4_E_ALIGN;
+    const int64_t ng = variant_groups(layers, nl, v.blocksize);
+    const size_t part = align256(size_t(ng) * sizeof(double));
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + 2 * part)) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table_variant(layers, nl, v.blocksize, ws, s)) != NF4_OK) return st;
+    char* w = static_cast<char*>(ws);
+    hipError_t e = nf4k::launch_variant_error(
+        reinterpret_cast<const LayerDesc*>(w), nl, ng, v.dtype, v.blocksize, v.dq_kind,
+        with_mean ? mean : nullptr, reinterpret_cast<double*>(w + table_bytes(nl)),
+        reinterpret_cast<double*>(w + table_bytes(nl) + part), err, s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
+                                  const float* mean, void* ws, size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_variant(v);
+    if (st != NF4_OK) return st;
+    const bool second = v.dq_kind != NF4_DQ_NONE, with_mean = v.dq_kind >= NF4_DQ_INT8_MEAN;
+    if (with_mean && !mean) return NF4_E_ARG;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl, NEED_CODES | NEED_OUT | (second ? NEED_Q | NEED_S2 : NEED_ABSMAX),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if (with_mean && !aligned(mean, 4)) return NF4_E_ALIGN;
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stage_table_variant(layers, nl, v.blocksize, ws, s)) != NF4_OK) return st;
+    hipError_t e = nf4k::launch_variant_dequant(static_cast<const LayerDesc*>(ws), nl,
+                                                variant_groups(layers, nl, v.blocksize), v.dtype,
+                                                v.blocksize, v.dq_kind, with_mean ? mean : nullptr, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 

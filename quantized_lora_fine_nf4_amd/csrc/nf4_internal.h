@@ -44,6 +44,15 @@ hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtyp
 // Standalone double quantisation of absmax.
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s);
 // Budgeted top-K; rank/perm are int32[nl] workspace arrays.
+// Codec variants (block 32/64/128/256; second-level kind 0 none, 1 int8,
+// 2 int8 minus the mean absmax, 3 E4M3 minus the mean absmax).  The table's
+// tile_end counts groups of 256 blocks of the variant's block size.
+// gsum and partial: one fp64 per group.
+hipError_t launch_variant_error(const LayerDesc* tab, int nl, int64_t ngroups, int dtype, int block,
+                                int kind, float* mean, double* gsum, double* partial, double* err,
+                                hipStream_t s);
+hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups, int dtype,
+                                  int block, int kind, const float* mean, hipStream_t s);
 // NF4 weight dequantised into the matmul that consumes it (bf16 MFMA):
 // forward out[m x rows] = x[m x cols] * W^T, backward out[m x cols] =
 // x[m x rows] * W; W [rows x cols] given by its codes and constants

@@ -261,3 +261,35 @@ def test_matmul_arguments():
     assert call(out=FAKE + 8) == q.NF4_E_ALIGN
     assert call(s2=FAKE + 2) == q.NF4_E_ALIGN
     assert L.nf4_matmul(None, rows, cols, f, 0, FAKE, 10, FAKE, 1, None) == q.NF4_E_ARG
+
+
+def test_variant_helpers_and_arguments():
+    for block in (32, 64, 128, 256):
+        for kind in range(4):
+            v = q.variant(q.NF4_BF16, block, kind)
+            for n in (1, 31, 4097, 70_778_880):
+                assert q.nf4_storage_bytes_variant(n, v) == oracle.storage_bytes_ex(n, block, kind)
+    assert q.nf4_storage_bytes_variant(100, q.variant(block=48)) == -1
+    assert q.nf4_storage_bytes_variant(100, q.variant(kind=4)) == -1
+    L = q.lib()
+    v = q.variant(q.NF4_BF16, 128, 3)
+    ns = [128 * 256 * 2 + 5]
+    need = q.nf4_workspace_bytes_variant(ns, v)
+    groups = 3
+    assert need == 256 + 2 * (((groups * 8) + 255) // 256) * 256
+
+    def call(layer=None, vv=v, mean=FAKE, err=FAKE, ws=FAKE, wsb=need):
+        arr = (q.nf4_layer * 1)(layer or _L(n=ns[0]))
+        return L.nf4_layer_error_variant(arr, 1, vv, mean, err, ws, wsb, None)
+    assert call(vv=q.variant(block=96)) == q.NF4_E_UNSUPPORTED
+    assert call(vv=q.variant(kind=7)) == q.NF4_E_UNSUPPORTED
+    assert call(mean=None) == q.NF4_E_ARG                        # kinds 2-3 write the mean
+    assert call(err=None) == q.NF4_E_ARG
+    assert call(layer=_L(n=ns[0], absmax=None)) == q.NF4_E_ARG    # absmax is always written
+    assert call(layer=_L(n=ns[0], qabsmax=None)) == q.NF4_E_ARG
+    assert call(mean=FAKE + 2) == q.NF4_E_ALIGN
+    assert call(err=FAKE + 4) == q.NF4_E_ALIGN
+    assert call(wsb=need - 1) == q.NF4_E_WORKSPACE
+    arr = (q.nf4_layer * 1)(_L(n=ns[0]))
+    assert L.nf4_dequantize_variant(arr, 1, v, None, FAKE, need, None) == q.NF4_E_ARG
+    assert L.nf4_dequantize_variant(arr, 1, q.variant(block=12), FAKE, FAKE, need, None) == q.NF4_E_UNSUPPORTED
