@@ -210,6 +210,51 @@ def variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes, r
     return res
 
 
+def codec_variants(q, torch, ls, cfg, stream, reps=5):
+    """The codec at block sizes 32-256 with each second-level kind on the
+    whole stack: the error pass (absmax, mean, second level, codes, error)
+    and the dequantisation.  Weights, codes and outputs are the stack's own
+    buffers; only the constants are allocated per block size.  GB/s count
+    the bytes the format must move per weight (16-bit weight, half a byte
+    of code, the stored constants), though the error pass reads the weights
+    twice (the mean of the kinds with an offset needs every absmax first)."""
+    nl = cfg.n_layers
+    n_total = cfg.total
+    err = torch.empty(nl, dtype=torch.float64, device="cuda")
+    mean = torch.empty(nl, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            e[2 * r].record(stream)
+            fn()
+            e[2 * r + 1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[2 * r].elapsed_time(e[2 * r + 1]) for r in range(reps)) / reps
+
+    kinds = (("none", q.NF4_DQ_NONE), ("int8", q.NF4_DQ_INT8),
+             ("int8_mean", q.NF4_DQ_INT8_MEAN), ("e4m3_mean", q.NF4_DQ_E4M3_MEAN))
+    res = {}
+    for block in (32, 64, 128, 256):
+        vs = q.LayerSet(cfg.sizes, q.fmt(cfg.dtype, True), with_absmax=True, w=ls.w,
+                        codes=ls.codes, out=ls.out, block=block)
+        ws = torch.empty(q.nf4_workspace_bytes_variant(vs.ns, q.variant(cfg.dtype, block, 0)),
+                         dtype=torch.uint8, device="cuda")
+        for kname, kind in kinds:
+            v = q.variant(cfg.dtype, block, kind)
+            store = sum(q.nf4_storage_bytes_variant(n, v) for n in cfg.sizes)
+            t_e = timed(lambda: q.nf4_layer_error_variant(vs, v, err, ws, mean=mean))
+            t_d = timed(lambda: q.nf4_dequantize_variant(vs, v, ws, mean=mean))
+            moved = 2.0 * n_total + store
+            res[f"b{block}_{kname}"] = {
+                "error_ms": round(t_e, 3), "error_GBps": round(moved / (t_e * 1e-3) / 1e9, 1),
+                "dequant_ms": round(t_d, 3), "dequant_GBps": round(moved / (t_d * 1e-3) / 1e9, 1),
+                "bits_per_weight": round(8.0 * store / n_total, 4)}
+        del vs, ws
+    return res
+
+
 MFMA_BF16_PEAK_TFS = 2500.0
 
 
@@ -308,7 +353,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip timing the selection variants after the steps")
+                    help="skip timing the selection variants, the fused matmul and the codec variants")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -477,6 +522,9 @@ def main():
             pb = fused_bytes if k == "nf4_layer_error" else deq_bytes
             pm = 0.5 * (out["protocol"][k]["ms_A"] + out["protocol"][k]["ms_A2"])
             out["protocol"][k]["GBps"] = round(pb / (pm * 1e-3) / 1e9, 1)
+    if not args.no_variants:   # last: it overwrites the stack's codes and outputs
+        log("timing the codec variants")
+        out["codec_variants"] = codec_variants(q, torch, ls, cfg, stream)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, n_deq, n_total)

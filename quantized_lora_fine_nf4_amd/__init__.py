@@ -303,11 +303,13 @@ class LayerSet:
     keeps the ABI's alignment (weights and outputs 16 B, codes 4 B).
     Attributes: ``w`` (int16 bits), ``codes`` (uint8), ``absmax`` (float32),
     ``qabsmax`` (int8), ``scale2`` (float32), ``out`` (int16 bits), the offset
-    lists ``*_off``, and ``c_layers`` (the nf4_layer array).
+    lists ``*_off``, and ``c_layers`` (the nf4_layer array).  ``w``, ``codes``
+    and ``out`` may be given (e.g. another LayerSet's, whose offsets do not
+    depend on the block size) instead of allocated.
     """
 
     def __init__(self, ns, f: nf4_format, device="cuda", with_out: bool = True,
-                 with_absmax: bool = True, w=None, block: int = BLOCK):
+                 with_absmax: bool = True, w=None, block: int = BLOCK, codes=None, out=None):
         import torch
         self.ns = [int(n) for n in ns]
         self.fmt = f
@@ -332,11 +334,19 @@ class LayerSet:
         else:
             assert w.dtype == torch.int16 and w.numel() >= wtot
             self.w = w
-        self.codes = torch.empty(ctot, dtype=torch.uint8, device=device)
+        if codes is None:
+            self.codes = torch.empty(ctot, dtype=torch.uint8, device=device)
+        else:
+            assert codes.dtype == torch.uint8 and codes.numel() >= ctot
+            self.codes = codes
         self.absmax = torch.empty(atot, dtype=torch.float32, device=device) if (with_absmax or not dq) else None
         self.qabsmax = torch.empty(atot, dtype=torch.int8, device=device) if dq else None
         self.scale2 = torch.empty(stot, dtype=torch.float32, device=device) if dq else None
-        self.out = torch.empty(wtot, dtype=torch.int16, device=device) if with_out else None
+        if out is not None:
+            assert out.dtype == torch.int16 and out.numel() >= wtot
+            self.out = out
+        else:
+            self.out = torch.empty(wtot, dtype=torch.int16, device=device) if with_out else None
         self._build()
 
     def _build(self):
