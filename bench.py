@@ -39,18 +39,27 @@ def algorithmic_bytes_per_weight(dq: bool) -> float:
     return 2.0 + 0.5 + ((1.0 / 64 + 4.0 / 16384) if dq else 4.0 / 64)
 
 
-def source_hash() -> str:
+# the files that define the fused codec and dequantisation kernels and their launches
+CODEC_SOURCES = ("k_codec.hip", "nf4_format.h", "nf4_internal.h")
+
+
+def source_hash(names=None) -> str:
+    """Hash of the kernel sources (all of them, or the named ones)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_lora_fine_nf4_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names if names is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
+def codec_source_hash() -> str:
+    return source_hash(CODEC_SOURCES)
+
+
 def read_traffic(workload_key: str, kernel: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel sources (else None)."""
+    on the current sources of the codec kernels (else None)."""
     path = os.path.join(PROFILES, f"traffic_{workload_key}.txt")
     if not os.path.exists(path):
         return None
@@ -59,7 +68,7 @@ def read_traffic(workload_key: str, kernel: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
+    if vals.get("codec_source_hash") != codec_source_hash():
         return None
     v = vals.get(f"{kernel}_bytes_per_launch")
     return float(v) if v else None
@@ -502,6 +511,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "source_hash": source_hash(),
+        "codec_source_hash": codec_source_hash(),
     }
     if not args.no_variants:
         out["variants"] = variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes)
