@@ -138,7 +138,9 @@ nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt,
 
 /* Dequantisation to the 16-bit type fmt.dtype.  Reads codes and either absmax
  * (dq_group == 0) or qabsmax + scale2 (dq_group == 256); writes out.
- * AQLoRA calls it for the layers that were not promoted. */
+ * AQLoRA calls it for the layers that were not promoted.  ws: at least the
+ * table and one 32-byte record per tile of these layers (nf4_workspace_bytes
+ * of them, or of any superset, is enough). */
 nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                           void* ws, size_t ws_bytes, void* stream);
 

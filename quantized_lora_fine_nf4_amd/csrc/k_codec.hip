@@ -655,40 +655,13 @@ __global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __res
 
 // ---- standalone dequantisation -------------------------------------------
 
-// Codes and constants of one tile for one lane: 8 dwords of packed codes
-// (8 weights each) and the raw constant of each dword's block.
-struct DqIn {
-    uint32_t c32[kLoads];
-    float own;   // constant of block 64 w + L: int8 qabsmax as float, or the fp32 absmax
-};
-
-template <bool DQ>
-__device__ __forceinline__ void load_dq(DqIn& r, const TileRef& tr)
-{
-    const LayerDesc& d = *tr.d;
-    const int valid = tr.valid;
-    const g_cu8 cp = (g_cu8)d.codes + (tr.e0 >> 1);
-    const uint32_t lb = lane_base();
-    if (valid == kTileElems) {
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) r.c32[j] = *(g_cu32)(cp + ((lb + j * 512u) >> 1));
-    } else {
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const uint32_t o = lb + j * 512u;
-            uint32_t c = 0;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-                if (o + 2 * bb < (uint32_t)valid) c |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
-            r.c32[j] = c;
-        }
-    }
-    // the lane's own block within the tile: wave w, lane L -> block 64 w + L
-    const uint32_t blk = threadIdx.x;
-    const bool in = (blk << 6) < (uint32_t)valid;
-    if constexpr (DQ) r.own = in ? (float)((g_ci8)d.qabsmax + (tr.e0 >> 6))[blk] : 0.0f;
-    else              r.own = in ? ((g_cf32)d.absmax + (tr.e0 >> 6))[blk] : 0.0f;
-}
+#ifndef NF4_DEQ_SPLIT
+#define NF4_DEQ_SPLIT 4              // workgroups per tile in the standalone dequantisation
+#endif
+constexpr int kDqSplit = NF4_DEQ_SPLIT;
+constexpr int kDqElems = kTileElems / kDqSplit;     // weights per workgroup
+constexpr int kDqSteps = kDqElems / (kThreads * 8); // 16-byte stores per thread
+static_assert(kDqSteps >= 1 && kDqSteps * kThreads * 8 * kDqSplit == kTileElems, "dequant split");
 
 template <typename T>
 __device__ __forceinline__ void store16(GLOBAL T* p, const T& v)
@@ -700,28 +673,107 @@ __device__ __forceinline__ void store16(GLOBAL T* p, const T& v)
 #endif
 }
 
-template <int DT, bool DQ>
-__device__ __forceinline__ void dequant_compute(const float* s_lv, const DqIn& r, const TileRef& tr)
+// Per-tile descriptor, built by k_dq_prep in the workspace before the
+// dequantisation: everything a workgroup needs about its tile in one 32-byte
+// record, read with scalar loads (no layer search in the hot kernel).
+struct alignas(32) DqTile {
+    const uint8_t* codes;   // the tile's first code byte
+    uint16_t* out;          // the tile's first output element
+    const void* cst;        // the tile's first int8 qabsmax, or fp32 absmax
+    float s2;               // the tile's scale2 (double quant), else unused
+    int32_t valid;          // elements of the tile inside the layer (1..16384)
+};
+static_assert(sizeof(DqTile) == kPartsPerTile * sizeof(double), "a record fits a tile's partials");
+
+// One thread per tile: find the layer (binary search over tile_end), write the record.
+template <bool DQ>
+__global__ __launch_bounds__(kThreads) void k_dq_prep(const LayerDesc* __restrict__ tab, int nl,
+                                                      int64_t ntiles, DqTile* __restrict__ desc)
 {
-    const int lane = threadIdx.x & 63;
-    const LayerDesc& d = *tr.d;
-    const int valid = tr.valid;
-    const g_u16 outp = (g_u16)d.out + tr.e0;
-    const float s2 = DQ ? ((g_cf32)d.scale2)[tr.local] : 1.0f;
-    const bool full = valid == kTileElems;
-    const uint32_t lb = lane_base();
+    const int64_t tile = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (tile >= ntiles) return;
+    const int l = first_layer(tab, nl, tile);
+    const LayerDesc& d = tab[l];
+    const int64_t local = tile - (d.tile_end - tiles_of(d.n));
+    const int64_t e0 = local << kTileShift;
+    const int64_t rem = d.n - e0;
+    DqTile r;
+    r.codes = d.codes + (e0 >> 1);
+    r.out = (uint16_t*)d.out + e0;
+    if constexpr (DQ) {
+        r.cst = d.qabsmax + (e0 >> 6);
+        r.s2 = ((g_cf32)d.scale2)[local];
+    } else {
+        r.cst = d.absmax + (e0 >> 6);
+        r.s2 = 0.0f;
+    }
+    r.valid = rem < kTileElems ? (int32_t)rem : kTileElems;
+    desc[tile] = r;
+}
+
+// A unit = 1/kDqSplit of a tile, one workgroup.  Step j of thread t covers the
+// 8 weights at 8 (256 j + t) of the unit, so at every step the workgroup writes
+// one contiguous 4 KB run of output; the 8 lanes 8m..8m+7 of a step share a
+// block, whose constant each lane loads itself (the same byte or word for the
+// 8 lanes).  Measured on the 14B-shaped stack in one process (bitwise equal
+// outputs): one workgroup per tile with 8 stores per thread and a layer search
+// 5.92 ms; quarter tiles from a tile record 5.35 ms; half tiles 5.59 ms;
+// eighth tiles 7.92 ms; quarter tiles from a tile-to-layer map and the layer
+// table 5.60 ms; an XCD-contiguous unit order changed nothing.  What made the
+// small workgroups pay off was issuing every load of a whole unit at once:
+// with the constant load behind a bounds guard each load was waited for in
+// its own branch, and the quarter tiles took 7.2 ms.
+template <int DT, bool DQ>
+__device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r, int sub)
+{
+    const int valid = r.valid - sub * kDqElems;
+    if (valid <= 0) return;   // past the end of a ragged last tile (the whole workgroup)
+    const g_cu8 cp = (g_cu8)r.codes + sub * (kDqElems / 2);
+    const g_u16 outp = (g_u16)r.out + (int64_t)sub * kDqElems;
+    const int b0 = sub * (kDqElems / 64);
+    const uint32_t t = threadIdx.x;
+    const bool full = valid >= kDqElems;
+    uint32_t c32[kDqSteps];
+    float k[kDqSteps];
+    if (full) {
+        // unconditional loads, all in flight at once (a guarded load would be
+        // waited for inside its branch)
+        int32_t qi[kDqSteps];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const uint32_t o = lb + j * 512u;
-        // block of this dword: 64 w + 8 j + L/8 -> held by lane 8 j + L/8 of the wave
-        const float kj = __builtin_bit_cast(float, __shfl(__builtin_bit_cast(int, r.own),
-                                                          8 * j + (lane >> 3), 64));
-        const float adq = DQ ? kj * s2 : kj;
+        for (int j = 0; j < kDqSteps; ++j) {
+            const uint32_t o = 8u * (j * (uint32_t)kThreads + t);
+            c32[j] = *(g_cu32)(cp + (o >> 1));
+            if constexpr (DQ) qi[j] = ((g_ci8)r.cst)[b0 + (o >> 6)];
+            else              k[j] = ((g_cf32)r.cst)[b0 + (o >> 6)];
+        }
+        if constexpr (DQ) {
+#pragma unroll
+            for (int j = 0; j < kDqSteps; ++j) k[j] = (float)qi[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kDqSteps; ++j) {
+            const uint32_t o = 8u * (j * (uint32_t)kThreads + t);
+            uint32_t c = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                if (o + 2 * bb < (uint32_t)valid) c |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
+            c32[j] = c;
+            const bool in = o < (uint32_t)valid;
+            if constexpr (DQ) k[j] = in ? (float)((g_ci8)r.cst)[b0 + (o >> 6)] : 0.0f;
+            else              k[j] = in ? ((g_cf32)r.cst)[b0 + (o >> 6)] : 0.0f;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();   // the wave's table writes precede its reads (LDS keeps a wave's order)
+#pragma unroll
+    for (int j = 0; j < kDqSteps; ++j) {
+        const uint32_t o = 8u * (j * (uint32_t)kThreads + t);
+        const float adq = DQ ? k[j] * r.s2 : k[j];
         uint32_t p[4];
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {
-            const float y0 = s_lv[(r.c32[j] >> (8 * k2)) & 15] * adq;
-            const float y1 = s_lv[(r.c32[j] >> (8 * k2 + 4)) & 15] * adq;
+            const float y0 = s_lv[(c32[j] >> (8 * k2)) & 15] * adq;
+            const float y1 = s_lv[(c32[j] >> (8 * k2 + 4)) & 15] * adq;
             float r0, r1;
             p[k2] = round_pair<DT>(y0, y1, r0, r1);
         }
@@ -730,33 +782,34 @@ __device__ __forceinline__ void dequant_compute(const float* s_lv, const DqIn& r
             store16((g_u4)(outp + o), pv);
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (o + k < (uint32_t)valid) outp[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
+            for (int kk = 0; kk < 8; ++kk)
+                if (o + kk < (uint32_t)valid) outp[o + kk] = (uint16_t)(p[kk >> 1] >> (16 * (kk & 1)));
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// One workgroup per tile: the dispatcher hands out tiles in index order, so
-// the tiles in flight stay one compact run of memory for the whole launch
-// (persistent workgroups drift apart and spread their stores).  Each wave
-// finds the layer and keeps its own copy of the level table, so the waves
-// never wait for each other.
+// One workgroup per unit, a one-shot grid: the dispatcher hands out units in
+// index order, so the units in flight stay one compact run of memory for the
+// whole launch (persistent workgroups drift apart and spread their stores).
+// Each wave keeps its own copy of the level table, so the waves never wait
+// for each other.
 template <int DT, bool DQ>
-__global__ __launch_bounds__(kThreads) void k_dequant(const LayerDesc* __restrict__ tab, int nl,
-                                                      int64_t first_tile)
+__global__ __launch_bounds__(kThreads) void k_dequant(const DqTile* __restrict__ desc, int64_t first_unit)
 {
     __shared__ float s_lv[kWaves][16];
     const int lane = threadIdx.x & 63;
     float* lv = s_lv[threadIdx.x >> 6];
-    if (lane < 16) lv[lane] = as_f(nf4fmt::kLevelBits[lane]);
-    const int64_t tile = first_tile + blockIdx.x;
-    int l = find_layer(tab, nl, tile);
-    const TileRef tr = tile_ref(tab, l, tile);
-    DqIn r;
-    load_dq<DQ>(r, tr);
-    __builtin_amdgcn_wave_barrier();   // the wave's table writes precede its reads (LDS keeps a wave's order)
-    dequant_compute<DT, DQ>(lv, r, tr);
+    if (lane < 16) {
+        // from immediates: a load of the table would be waited for before the first data load
+        float v = as_f(nf4fmt::kLevelBits[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) v = lane == i ? as_f(nf4fmt::kLevelBits[i]) : v;
+        lv[lane] = v;
+    }
+    const int64_t unit = first_unit + blockIdx.x;
+    const int64_t tile = unit / kDqSplit;
+    const DqTile r = desc[tile];   // uniform: scalar loads
+    dequant_unit<DT, DQ>(lv, r, (int)(unit - tile * kDqSplit));
 }
 
 // ---- standalone double quantisation --------------------------------------
@@ -861,11 +914,19 @@ hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, d
 constexpr int64_t kMaxGrid = (int64_t(1) << 32) / kThreads - 1;
 
 template <int DT, bool DQ>
-hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)
+hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, void* desc_ws, hipStream_t s)
 {
-    for (int64_t t0 = 0; t0 < ntiles; t0 += kMaxGrid) {
-        const int64_t g = ntiles - t0 < kMaxGrid ? ntiles - t0 : kMaxGrid;
-        hipLaunchKernelGGL((k_dequant<DT, DQ>), dim3((unsigned)g), dim3(kThreads), 0, s, tab, nl, t0);
+    DqTile* desc = static_cast<DqTile*>(desc_ws);
+    if (ntiles > kMaxGrid * kThreads) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_dq_prep<DQ>), dim3((unsigned)((ntiles + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, s, tab, nl, ntiles, desc);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    const int64_t nunits = ntiles * kDqSplit;
+    for (int64_t t0 = 0; t0 < nunits; t0 += kMaxGrid) {
+        const int64_t g = nunits - t0 < kMaxGrid ? nunits - t0 : kMaxGrid;
+        hipLaunchKernelGGL((k_dequant<DT, DQ>), dim3((unsigned)g), dim3(kThreads), 0, s,
+                           (const DqTile*)desc, t0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -896,11 +957,12 @@ hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, do
 }
 
 hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                          hipStream_t s)
+                          void* desc_ws, hipStream_t s)
 {
-    if (dtype == 0) return dq ? dequant_go<0, true>(tab, nl, ntiles, s)
-                              : dequant_go<0, false>(tab, nl, ntiles, s);
-    return dq ? dequant_go<1, true>(tab, nl, ntiles, s) : dequant_go<1, false>(tab, nl, ntiles, s);
+    if (dtype == 0) return dq ? dequant_go<0, true>(tab, nl, ntiles, desc_ws, s)
+                              : dequant_go<0, false>(tab, nl, ntiles, desc_ws, s);
+    return dq ? dequant_go<1, true>(tab, nl, ntiles, desc_ws, s)
+              : dequant_go<1, false>(tab, nl, ntiles, desc_ws, s);
 }
 
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)

@@ -297,11 +297,12 @@ nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, v
     st = check_layers(layers, nl, NEED_CODES | NEED_OUT | (dq ? NEED_Q | NEED_S2 : NEED_ABSMAX),
                       &ntiles);
     if (st != NF4_OK) return st;
-    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    // the table, then one 32-byte record per tile (where the fused pass keeps its partials)
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + partial_bytes(ntiles))) != NF4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_dequant(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype,
-                                        dq, s);
+                                        dq, static_cast<char*>(ws) + table_bytes(nl), s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 

@@ -38,9 +38,10 @@ hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragge
 // Per-layer fixed-order sum of the per-tile partials into err[nl].
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
                          hipStream_t s);
-// Standalone dequantisation (qabsmax/scale2 when dq, else absmax).
+// Standalone dequantisation (qabsmax/scale2 when dq, else absmax); desc_ws:
+// device scratch for one 32-byte record per tile (kPartsPerTile doubles).
 hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                          hipStream_t s);
+                          void* desc_ws, hipStream_t s);
 // Standalone double quantisation of absmax.
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s);
 // Budgeted top-K; rank/perm are int32[nl] workspace arrays.
