@@ -278,6 +278,38 @@ def test_host_layer_array_may_be_reused_at_once():
         compare_layer(ls, i, w, q.NF4_BF16, True)
 
 
+@pytest.mark.parametrize("call", ["nf4_quantize", "nf4_dequantize", "nf4_layer_error"])
+def test_workspace_writes_stay_inside_the_minimum_size(call):
+    """Each call given exactly the smallest workspace it accepts, followed by a
+    guard region: the guard is untouched and the outputs are right."""
+    f = q.fmt(q.NF4_BF16, True)
+    ws_list = [synth.generate_raw(80 + i, n) for i, n in enumerate([16384 * 3 + 5, 100, 16384 * 7])]
+    ls = layerset(ws_list, f)
+    nl, ntiles = len(ls), sum((n + 16383) // 16384 for n in ls.ns)
+    table = (nl * 64 + 255) // 256 * 256
+    need = table if call == "nf4_quantize" else table + (ntiles * 32 + 255) // 256 * 256
+    guard = 4096
+    buf = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    err = torch.empty(nl, dtype=torch.float64, device="cuda")
+    L, st = q.lib(), torch.cuda.current_stream().cuda_stream
+    if call == "nf4_dequantize":   # codes and constants from a full-size workspace first
+        q.nf4_layer_error(ls, f, err, workspace(ls.ns, f))
+        torch.cuda.synchronize()
+        ls.out.view(torch.uint8).fill_(0x5A)
+    args = (ls.c_layers, nl, f)
+    if call == "nf4_layer_error":
+        assert L.nf4_layer_error(*args, err.data_ptr(), buf.data_ptr(), need - 1, st) == q.NF4_E_WORKSPACE
+        rc = L.nf4_layer_error(*args, err.data_ptr(), buf.data_ptr(), need, st)
+    else:
+        assert getattr(L, call)(*args, buf.data_ptr(), need - 1, st) == q.NF4_E_WORKSPACE
+        rc = getattr(L, call)(*args, buf.data_ptr(), need, st)
+    assert rc == q.NF4_OK
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all())
+    for i, w in enumerate(ws_list):
+        compare_layer(ls, i, w, q.NF4_BF16, True, check_out=(call == "nf4_dequantize"))
+
+
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("nl", [1, 2, 7, 300, 1025, 4097, 65536])
 def test_select_matches_oracle_on_the_same_scores(nl):
