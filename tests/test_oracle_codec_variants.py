@@ -142,3 +142,33 @@ def test_bit_accounting():
     # the mean costs one fp32 per matrix
     for k in (K2, K3):
         assert oracle.storage_bytes_ex(n, 64, k) == oracle.storage_bytes_ex(n, 64, K1) + 4
+
+
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("kind", [K1, K2, K3])
+def test_group_maximum_takes_the_top_code(block, kind):
+    """In every group with a nonzero |c| maximum, the block holding it maps to
+    the second level's largest value: 127 for the int8 kinds, 448 for E4M3
+    (so s2 is that maximum over 127 or 448, not some other divisor), and
+    every other block stays within it."""
+    w = synth.generate_raw(900 + kind + block, block * 256 * 5 + 3 * block + 7, dtype=BF16,
+                           outlier_frac=0.003)
+    r = oracle.layer_error_ex(w, BF16, block, kind)
+    a = r["absmax"].astype(np.float64)
+    c = a - (r["mean"] if kind != K1 else 0.0)
+    if kind == K3:
+        qv = np.array([oracle.e4m3_decode(int(b)) for b in r["q"]], np.float64)
+        top = 448.0
+    else:
+        qv = r["q"].view(np.int8).astype(np.float64)
+        top = 127.0
+    ng = r["scale2"].size
+    for g in range(ng):
+        sl = slice(256 * g, min(256 * (g + 1), a.size))
+        cg, qg = np.abs(c[sl]), np.abs(qv[sl])
+        if cg.max() == 0:
+            assert r["scale2"][g] == 0 and not qg.any()
+            continue
+        assert qg[int(np.argmax(cg))] == top, g
+        assert qg.max() == top, g
+        assert r["scale2"][g] == np.float32(np.float32(cg.max()) / np.float32(top)), g
