@@ -659,9 +659,13 @@ __global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __res
 #define NF4_DEQ_SPLIT 4              // workgroups per tile in the standalone dequantisation
 #endif
 constexpr int kDqSplit = NF4_DEQ_SPLIT;
-constexpr int kDqElems = kTileElems / kDqSplit;     // weights per workgroup
-constexpr int kDqSteps = kDqElems / (kThreads * 8); // 16-byte stores per thread
-static_assert(kDqSteps >= 1 && kDqSteps * kThreads * 8 * kDqSplit == kTileElems, "dequant split");
+#ifndef NF4_DEQ_THREADS
+#define NF4_DEQ_THREADS 128          // threads per dequantisation workgroup
+#endif
+constexpr int kDqThreads = NF4_DEQ_THREADS;
+constexpr int kDqElems = kTileElems / kDqSplit;       // weights per workgroup
+constexpr int kDqSteps = kDqElems / (kDqThreads * 8); // 16-byte stores per thread
+static_assert(kDqSteps >= 1 && kDqSteps * kDqThreads * 8 * kDqSplit == kTileElems, "dequant split");
 
 template <typename T>
 __device__ __forceinline__ void store16(GLOBAL T* p, const T& v)
@@ -711,18 +715,21 @@ __global__ __launch_bounds__(kThreads) void k_dq_prep(const LayerDesc* __restric
     desc[tile] = r;
 }
 
-// A unit = 1/kDqSplit of a tile, one workgroup.  Step j of thread t covers the
-// 8 weights at 8 (256 j + t) of the unit, so at every step the workgroup writes
-// one contiguous 4 KB run of output; the 8 lanes 8m..8m+7 of a step share a
-// block, whose constant each lane loads itself (the same byte or word for the
-// 8 lanes).  Measured on the 14B-shaped stack in one process (bitwise equal
-// outputs): one workgroup per tile with 8 stores per thread and a layer search
-// 5.92 ms; quarter tiles from a tile record 5.35 ms; half tiles 5.59 ms;
-// eighth tiles 7.92 ms; quarter tiles from a tile-to-layer map and the layer
-// table 5.60 ms; an XCD-contiguous unit order changed nothing.  What made the
-// small workgroups pay off was issuing every load of a whole unit at once:
-// with the constant load behind a bounds guard each load was waited for in
-// its own branch, and the quarter tiles took 7.2 ms.
+// A unit = 1/kDqSplit of a tile, one workgroup of T = kDqThreads threads.
+// Step j of thread t covers the 8 weights at 8 (T j + t) of the unit, so at
+// every step the workgroup writes one contiguous 16 T-byte run of output; the
+// 8 lanes 8m..8m+7 of a step share a block, whose constant each lane loads
+// itself (the same byte or word for the 8 lanes).  Measured on the 14B-shaped
+// stack in one process (bitwise equal outputs): one 256-thread workgroup per
+// tile with 8 stores per thread and a layer search 5.92 ms; from a tile
+// record, 256 threads: quarter tiles 5.35 ms, half 5.59, eighth 7.92; quarter
+// tiles from a tile-to-layer map and the layer table 5.60 ms; 128 threads:
+// quarter tiles (4 stores per thread) 5.07 ms, half 5.99, whole 6.00; 64
+// threads: eighth tiles (4 stores) 5.07, quarter 5.97, sixteenth 5.67; 512
+// threads: half 5.41, quarter 7.70; an XCD-contiguous unit order changed
+// nothing.  What made the small workgroups pay off at all was issuing every
+// load of a whole unit at once: with the constant load behind a bounds guard
+// each load was waited for in its own branch, and quarter tiles took 7.2 ms.
 template <int DT, bool DQ>
 __device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r, int sub)
 {
@@ -741,7 +748,7 @@ __device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r,
         int32_t qi[kDqSteps];
 #pragma unroll
         for (int j = 0; j < kDqSteps; ++j) {
-            const uint32_t o = 8u * (j * (uint32_t)kThreads + t);
+            const uint32_t o = 8u * (j * (uint32_t)kDqThreads + t);
             c32[j] = *(g_cu32)(cp + (o >> 1));
             if constexpr (DQ) qi[j] = ((g_ci8)r.cst)[b0 + (o >> 6)];
             else              k[j] = ((g_cf32)r.cst)[b0 + (o >> 6)];
@@ -753,7 +760,7 @@ __device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r,
     } else {
 #pragma unroll
         for (int j = 0; j < kDqSteps; ++j) {
-            const uint32_t o = 8u * (j * (uint32_t)kThreads + t);
+            const uint32_t o = 8u * (j * (uint32_t)kDqThreads + t);
             uint32_t c = 0;
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
@@ -767,7 +774,7 @@ __device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r,
     __builtin_amdgcn_wave_barrier();   // the wave's table writes precede its reads (LDS keeps a wave's order)
 #pragma unroll
     for (int j = 0; j < kDqSteps; ++j) {
-        const uint32_t o = 8u * (j * (uint32_t)kThreads + t);
+        const uint32_t o = 8u * (j * (uint32_t)kDqThreads + t);
         const float adq = DQ ? k[j] * r.s2 : k[j];
         uint32_t p[4];
 #pragma unroll
@@ -794,9 +801,9 @@ __device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r,
 // Each wave keeps its own copy of the level table, so the waves never wait
 // for each other.
 template <int DT, bool DQ>
-__global__ __launch_bounds__(kThreads) void k_dequant(const DqTile* __restrict__ desc, int64_t first_unit)
+__global__ __launch_bounds__(kDqThreads) void k_dequant(const DqTile* __restrict__ desc, int64_t first_unit)
 {
-    __shared__ float s_lv[kWaves][16];
+    __shared__ float s_lv[kDqThreads / 64][16];
     const int lane = threadIdx.x & 63;
     float* lv = s_lv[threadIdx.x >> 6];
     if (lane < 16) {
@@ -923,9 +930,10 @@ hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, void* desc_w
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     const int64_t nunits = ntiles * kDqSplit;
-    for (int64_t t0 = 0; t0 < nunits; t0 += kMaxGrid) {
-        const int64_t g = nunits - t0 < kMaxGrid ? nunits - t0 : kMaxGrid;
-        hipLaunchKernelGGL((k_dequant<DT, DQ>), dim3((unsigned)g), dim3(kThreads), 0, s,
+    constexpr int64_t kMaxDqGrid = (int64_t(1) << 32) / kDqThreads - 1;
+    for (int64_t t0 = 0; t0 < nunits; t0 += kMaxDqGrid) {
+        const int64_t g = nunits - t0 < kMaxDqGrid ? nunits - t0 : kMaxDqGrid;
+        hipLaunchKernelGGL((k_dequant<DT, DQ>), dim3((unsigned)g), dim3(kDqThreads), 0, s,
                            (const DqTile*)desc, t0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
