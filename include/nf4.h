@@ -231,7 +231,9 @@ nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_vari
                                    void* stream);
 
 /* Dequantisation of a variant's codes: reads codes, absmax (kind 0) or
- * qabsmax + scale2 (+ mean for kinds 2-3); writes out (16-byte aligned). */
+ * qabsmax + scale2 (+ mean for kinds 2-3); writes out (16-byte aligned).
+ * ws: at least the table and one 64-byte record per group of these layers
+ * (nf4_workspace_bytes_variant of them, or of any superset, is enough). */
 nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
                                   const float* mean, void* ws, size_t ws_bytes, void* stream);
 
@@ -265,7 +267,8 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
 size_t      nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format fmt);
 /* Workspace for aqlora_select_topk and aqlora_select; 0 on bad input. */
 size_t      aqlora_workspace_bytes(int32_t nl);
-/* Workspace for the variant calls (table + two fp64 per group); 0 on bad input. */
+/* Workspace for the variant calls (the table, then the larger of two fp64 per
+ * group and one 64-byte record per group); 0 on bad input. */
 size_t      nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_variant v);
 /* ceil(n/2) + (kind 0 ? 4 nb : nb + 4 ng) + (kinds 2-3 ? 4 : 0); -1 on bad input. */
 int64_t     nf4_storage_bytes_variant(int64_t n, nf4_variant v);

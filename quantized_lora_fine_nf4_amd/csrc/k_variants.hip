@@ -576,64 +576,111 @@ __global__ __launch_bounds__(kVThreads, 4) void k_var_codec(const LayerDesc* __r
 }
 
 // ---- standalone dequantisation ---------------------------------------------
+//
+// A prep kernel writes one 64-byte record per group (its codes, output and
+// constants, scale2, the matrix's mean, the valid count); then 128-thread
+// workgroups each take 4,096 weights of a group (a unit) with four 16-byte
+// stores per thread, every load of a whole unit issued at once -- the shape
+// that measured fastest for the main dequantisation.
 
-template <int DT, int B, bool FULL>
-__device__ __forceinline__ void dequant_body(const float* s_lv, const float* s_adq, const VGroup& g)
+struct alignas(64) VarDqRec {
+    const uint8_t* codes;   // the group's first code byte
+    uint16_t* out;          // the group's first output element
+    const void* cst;        // the group's first stored constant (byte, or fp32 absmax)
+    float s2;               // the group's scale2 (kinds 1-3)
+    float mu;               // the matrix's mean absmax (kinds 2-3)
+    int32_t valid;          // elements of the group inside the matrix
+};
+constexpr int kVdThreads = 128;
+constexpr int kVdUnit = 4096;                        // weights per workgroup
+constexpr int kVdSteps = kVdUnit / (kVdThreads * 8); // 16-byte stores per thread
+
+template <int B, int KIND>
+__global__ __launch_bounds__(256) void k_var_dq_prep(const LayerDesc* __restrict__ tab, int nl,
+                                                     int64_t ngroups, const float* __restrict__ mean,
+                                                     VarDqRec* __restrict__ rec)
 {
-    constexpr int NL = B / 8;
-    const GLOBAL uint8_t* cp = (const GLOBAL uint8_t*)g.d->codes + (g.e0 >> 1);
-    GLOBAL uint16_t* out = (GLOBAL uint16_t*)g.d->out + g.e0;
-#pragma unroll 4
-    for (int j = 0; j < NL; ++j) {
-        const uint32_t o = voff<B>(j);
-        if (!FULL && (int)o >= g.valid) continue;
-        const bool whole = FULL || (int)o + 8 <= g.valid;
-        uint32_t cw = 0;
-        if (whole) {
-            cw = *(const GLOBAL uint32_t*)(cp + (o >> 1));
-        } else {
-            const int nbytes = (g.valid - (int)o + 1) >> 1;
-            for (int bb = 0; bb < nbytes; ++bb) cw |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
-        }
-        const float adq = s_adq[vblock<B>(j)];
-        uint32_t p[4];
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2)
-            p[k2] = round_pair<DT>(s_lv[(cw >> (8 * k2)) & 15] * adq, s_lv[(cw >> (8 * k2 + 4)) & 15] * adq);
-        if (whole) {
-            *(GLOBAL u32x4*)(out + o) = u32x4{p[0], p[1], p[2], p[3]};
-        } else {
-            for (int k = 0; k < 8; ++k)
-                if ((int)o + k < g.valid) out[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
-        }
-    }
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gi >= ngroups) return;
+    const VGroup g = vgroup<B>(tab, nl, gi);
+    const LayerDesc& d = *g.d;
+    VarDqRec r;
+    r.codes = d.codes + (g.e0 >> 1);
+    r.out = (uint16_t*)d.out + g.e0;
+    const int64_t b0 = g.local * kVThreads;
+    r.cst = KIND == 0 ? (const void*)(d.absmax + b0) : (const void*)((const uint8_t*)d.qabsmax + b0);
+    r.s2 = KIND == 0 ? 0.0f : ((const GLOBAL float*)d.scale2)[g.local];
+    r.mu = KIND >= 2 ? mean[g.l] : 0.0f;
+    r.valid = g.valid;
+    rec[gi] = r;
 }
 
 template <int DT, int B, int KIND>
-__global__ __launch_bounds__(kVThreads) void k_var_dequant(const LayerDesc* __restrict__ tab, int nl,
-                                                           const float* __restrict__ mean)
+__global__ __launch_bounds__(kVdThreads) void k_var_dequant(const VarDqRec* __restrict__ rec,
+                                                            int64_t first_unit)
 {
-    __shared__ float s_lv[16];
-    __shared__ float s_adq[kVThreads];
-    const int t = threadIdx.x;
-    if (t < 16) s_lv[t] = as_f(nf4fmt::kLevelBits[t]);
-    const VGroup g = vgroup<B>(tab, nl, blockIdx.x);
-    const LayerDesc& d = *g.d;
-    const int64_t b = g.local * kVThreads + t;
-    float adq = 0.0f;
-    if (t < g.nbv) {
-        if constexpr (KIND == 0) {
-            adq = ((const GLOBAL float*)d.absmax)[b];
-        } else {
-            const uint32_t q = ((const GLOBAL uint8_t*)d.qabsmax)[b];
-            const float s2 = ((const GLOBAL float*)d.scale2)[g.local];
-            adq = block_adq<KIND>(0.0f, q, s2, KIND >= 2 ? mean[g.l] : 0.0f);
+    constexpr int UPG = kVThreads * B / kVdUnit;   // units per group
+    __shared__ float s_lv[kVdThreads / 64][16];
+    const int t = threadIdx.x, lane = t & 63;
+    float* lv = s_lv[t >> 6];
+    if (lane < 16) {   // from immediates: no load before the data loads
+        float v = as_f(nf4fmt::kLevelBits[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) v = lane == i ? as_f(nf4fmt::kLevelBits[i]) : v;
+        lv[lane] = v;
+    }
+    const int64_t unit = first_unit + blockIdx.x;
+    const int64_t gi = unit / UPG;
+    const int sub = (int)(unit - gi * UPG);
+    const VarDqRec r = rec[gi];   // uniform: scalar loads
+    const int valid = r.valid - sub * kVdUnit;
+    if (valid <= 0) return;       // past the end of a ragged last group (the whole workgroup)
+    const GLOBAL uint8_t* cp = (const GLOBAL uint8_t*)r.codes + sub * (kVdUnit / 2);
+    GLOBAL uint16_t* out = (GLOBAL uint16_t*)r.out + (int64_t)sub * kVdUnit;
+    const int bsub = sub * (kVdUnit / B);          // first block of the unit within the group
+    const bool full = valid >= kVdUnit;
+    uint32_t cw[kVdSteps];
+    uint32_t raw[kVdSteps];
+    if (full) {
+#pragma unroll
+        for (int j = 0; j < kVdSteps; ++j) {
+            const uint32_t o = 8u * (j * (uint32_t)kVdThreads + t);
+            cw[j] = *(const GLOBAL uint32_t*)(cp + (o >> 1));
+            const int bl = bsub + (int)(o / B);
+            raw[j] = KIND == 0 ? as_u(((const GLOBAL float*)r.cst)[bl])
+                               : (uint32_t)((const GLOBAL uint8_t*)r.cst)[bl];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVdSteps; ++j) {
+            const uint32_t o = 8u * (j * (uint32_t)kVdThreads + t);
+            uint32_t c = 0;
+            for (int bb = 0; bb < 4; ++bb)
+                if ((int)o + 2 * bb < valid) c |= (uint32_t)cp[(o >> 1) + bb] << (8 * bb);
+            cw[j] = c;
+            const int bl = bsub + (int)(o / B);
+            raw[j] = (int)o < valid ? (KIND == 0 ? as_u(((const GLOBAL float*)r.cst)[bl])
+                                                 : (uint32_t)((const GLOBAL uint8_t*)r.cst)[bl])
+                                    : 0u;
         }
     }
-    s_adq[t] = adq;
-    __syncthreads();
-    if (g.valid == kVThreads * B) dequant_body<DT, B, true>(s_lv, s_adq, g);
-    else dequant_body<DT, B, false>(s_lv, s_adq, g);
+    __builtin_amdgcn_wave_barrier();   // the wave's table writes precede its reads (LDS keeps a wave's order)
+#pragma unroll
+    for (int j = 0; j < kVdSteps; ++j) {
+        const uint32_t o = 8u * (j * (uint32_t)kVdThreads + t);
+        if (!full && (int)o >= valid) continue;
+        const float adq = KIND == 0 ? as_f(raw[j]) : block_adq<KIND>(0.0f, raw[j], r.s2, r.mu);
+        uint32_t p[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2)
+            p[k2] = round_pair<DT>(lv[(cw[j] >> (8 * k2)) & 15] * adq, lv[(cw[j] >> (8 * k2 + 4)) & 15] * adq);
+        if (full || (int)o + 8 <= valid) {
+            *(GLOBAL u32x4*)(out + o) = u32x4{p[0], p[1], p[2], p[3]};
+        } else {
+            for (int k = 0; k < 8; ++k)
+                if ((int)o + k < valid) out[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
+        }
+    }
 }
 
 // per-matrix sum of the group partials, one workgroup per matrix (a fixed
@@ -692,12 +739,25 @@ hipError_t variant_go(const LayerDesc* tab, int nl, int64_t ngroups, float* mean
 }
 
 template <int DT, int B, int KIND>
-hipError_t variant_dq_go(const LayerDesc* tab, int nl, int64_t ngroups, const float* mean, hipStream_t s)
+hipError_t variant_dq_go(const LayerDesc* tab, int nl, int64_t ngroups, const float* mean,
+                         void* rec_ws, hipStream_t s)
 {
     if (ngroups > kMaxVGrid) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_var_dequant<DT, B, KIND>), dim3((unsigned)ngroups), dim3(kVThreads), 0, s,
-                       tab, nl, mean);
-    return hipGetLastError();
+    VarDqRec* rec = static_cast<VarDqRec*>(rec_ws);
+    hipLaunchKernelGGL((k_var_dq_prep<B, KIND>), dim3((unsigned)((ngroups + 255) / 256)), dim3(256), 0, s,
+                       tab, nl, ngroups, mean, rec);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int64_t UPG = kVThreads * B / kVdUnit;
+    constexpr int64_t kMaxUnits = (int64_t(1) << 32) / kVdThreads - 1;
+    const int64_t nunits = ngroups * UPG;
+    for (int64_t u0 = 0; u0 < nunits; u0 += kMaxUnits) {
+        const int64_t n = nunits - u0 < kMaxUnits ? nunits - u0 : kMaxUnits;
+        hipLaunchKernelGGL((k_var_dequant<DT, B, KIND>), dim3((unsigned)n), dim3(kVdThreads), 0, s,
+                           (const VarDqRec*)rec, u0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DT, int B>
@@ -714,13 +774,13 @@ hipError_t variant_kind(const LayerDesc* tab, int nl, int64_t ng, int kind, floa
 
 template <int DT, int B>
 hipError_t variant_dq_kind(const LayerDesc* tab, int nl, int64_t ng, int kind, const float* mean,
-                           hipStream_t s)
+                           void* rec, hipStream_t s)
 {
     switch (kind) {
-        case 0: return variant_dq_go<DT, B, 0>(tab, nl, ng, mean, s);
-        case 1: return variant_dq_go<DT, B, 1>(tab, nl, ng, mean, s);
-        case 2: return variant_dq_go<DT, B, 2>(tab, nl, ng, mean, s);
-        default: return variant_dq_go<DT, B, 3>(tab, nl, ng, mean, s);
+        case 0: return variant_dq_go<DT, B, 0>(tab, nl, ng, mean, rec, s);
+        case 1: return variant_dq_go<DT, B, 1>(tab, nl, ng, mean, rec, s);
+        case 2: return variant_dq_go<DT, B, 2>(tab, nl, ng, mean, rec, s);
+        default: return variant_dq_go<DT, B, 3>(tab, nl, ng, mean, rec, s);
     }
 }
 
@@ -739,13 +799,13 @@ hipError_t variant_block(const LayerDesc* tab, int nl, int64_t ng, int block, in
 
 template <int DT>
 hipError_t variant_dq_block(const LayerDesc* tab, int nl, int64_t ng, int block, int kind,
-                            const float* mean, hipStream_t s)
+                            const float* mean, void* rec, hipStream_t s)
 {
     switch (block) {
-        case 32: return variant_dq_kind<DT, 32>(tab, nl, ng, kind, mean, s);
-        case 64: return variant_dq_kind<DT, 64>(tab, nl, ng, kind, mean, s);
-        case 128: return variant_dq_kind<DT, 128>(tab, nl, ng, kind, mean, s);
-        case 256: return variant_dq_kind<DT, 256>(tab, nl, ng, kind, mean, s);
+        case 32: return variant_dq_kind<DT, 32>(tab, nl, ng, kind, mean, rec, s);
+        case 64: return variant_dq_kind<DT, 64>(tab, nl, ng, kind, mean, rec, s);
+        case 128: return variant_dq_kind<DT, 128>(tab, nl, ng, kind, mean, rec, s);
+        case 256: return variant_dq_kind<DT, 256>(tab, nl, ng, kind, mean, rec, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -761,10 +821,10 @@ hipError_t launch_variant_error(const LayerDesc* tab, int nl, int64_t ngroups, i
 }
 
 hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups, int dtype,
-                                  int block, int kind, const float* mean, hipStream_t s)
+                                  int block, int kind, const float* mean, void* rec_ws, hipStream_t s)
 {
-    if (dtype == 0) return variant_dq_block<0>(tab, nl, ngroups, block, kind, mean, s);
-    return variant_dq_block<1>(tab, nl, ngroups, block, kind, mean, s);
+    if (dtype == 0) return variant_dq_block<0>(tab, nl, ngroups, block, kind, mean, rec_ws, s);
+    return variant_dq_block<1>(tab, nl, ngroups, block, kind, mean, rec_ws, s);
 }
 
 }  // namespace nf4k

@@ -133,6 +133,14 @@ nf4_status check_variant(const nf4_variant& v)
     return NF4_OK;
 }
 
+// Workspace after the table for the variant calls: two fp64 per group (error
+// pass) or one 64-byte record per group (dequantisation), whichever is larger.
+size_t variant_scratch_bytes(int64_t ng)
+{
+    const size_t two = 2 * align256(size_t(ng) * sizeof(double)), rec = align256(size_t(ng) * 64);
+    return two > rec ? two : rec;
+}
+
 int64_t variant_groups(const nf4_layer* L, int32_t nl, int block)
 {
     int64_t g = 0;
@@ -409,7 +417,7 @@ size_t nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_v
         if (n_per_layer[i] <= 0 || n_per_layer[i] >= kMaxN) return 0;
         g += ((n_per_layer[i] + v.blocksize - 1) / v.blocksize + nf4fmt::kGroup - 1) / nf4fmt::kGroup;
     }
-    return table_bytes(nl) + 2 * align256(size_t(g) * sizeof(double));
+    return table_bytes(nl) + variant_scratch_bytes(g);
 }
 
 int64_t nf4_storage_bytes_variant(int64_t n, nf4_variant v)
@@ -460,12 +468,13 @@ nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_varia
                       &ntiles);
     if (st != NF4_OK) return st;
     if (with_mean && !aligned(mean, 4)) return NF4_E_ALIGN;
-    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    const int64_t ng = variant_groups(layers, nl, v.blocksize);
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + align256(size_t(ng) * 64))) != NF4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stage_table_variant(layers, nl, v.blocksize, ws, s)) != NF4_OK) return st;
-    hipError_t e = nf4k::launch_variant_dequant(static_cast<const LayerDesc*>(ws), nl,
-                                                variant_groups(layers, nl, v.blocksize), v.dtype,
-                                                v.blocksize, v.dq_kind, with_mean ? mean : nullptr, s);
+    hipError_t e = nf4k::launch_variant_dequant(static_cast<const LayerDesc*>(ws), nl, ng, v.dtype,
+                                                v.blocksize, v.dq_kind, with_mean ? mean : nullptr,
+                                                static_cast<char*>(ws) + table_bytes(nl), s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 

@@ -52,8 +52,9 @@ hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hip
 hipError_t launch_variant_error(const LayerDesc* tab, int nl, int64_t ngroups, int dtype, int block,
                                 int kind, float* mean, double* gsum, double* partial, double* err,
                                 hipStream_t s);
+// rec_ws: device scratch for one 64-byte record per group.
 hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups, int dtype,
-                                  int block, int kind, const float* mean, hipStream_t s);
+                                  int block, int kind, const float* mean, void* rec_ws, hipStream_t s);
 // NF4 weight dequantised into the matmul that consumes it (bf16 MFMA):
 // forward out[m x rows] = x[m x cols] * W^T, backward out[m x cols] =
 // x[m x rows] * W; W [rows x cols] given by its codes and constants

@@ -277,7 +277,7 @@ def test_variant_helpers_and_arguments():
     ns = [128 * 256 * 2 + 5]
     need = q.nf4_workspace_bytes_variant(ns, v)
     groups = 3
-    assert need == 256 + 2 * (((groups * 8) + 255) // 256) * 256
+    assert need == 256 + max(2 * (((groups * 8) + 255) // 256) * 256, ((groups * 64) + 255) // 256 * 256)
 
     def call(layer=None, vv=v, mean=FAKE, err=FAKE, ws=FAKE, wsb=need):
         arr = (q.nf4_layer * 1)(layer or _L(n=ns[0]))
