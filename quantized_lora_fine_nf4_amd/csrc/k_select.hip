@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include "nf4_internal.h"
+#include "nf4_launch.h"
 
 namespace nf4k {
 namespace {

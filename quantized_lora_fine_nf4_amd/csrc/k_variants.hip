@@ -38,6 +38,7 @@
 
 #include "nf4_format.h"
 #include "nf4_internal.h"
+#include "nf4_launch.h"
 
 namespace nf4k {
 namespace {

@@ -10,6 +10,7 @@
 
 #include "nf4_format.h"
 #include "nf4_internal.h"
+#include "nf4_launch.h"
 
 using nf4k::LayerDesc;
 

@@ -1,5 +1,6 @@
-// nf4_internal.h -- device-side layer table and kernel launchers (not part of
-// the public ABI; the C entry points in nf4_api.cpp validate and call these).
+// nf4_internal.h -- the device-side layer table and the tile constants shared
+// by the kernels and the C entry points (not part of the public ABI).  The
+// launchers are declared in nf4_launch.h.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,57 +28,5 @@ struct LayerDesc {
 static_assert(sizeof(LayerDesc) == 64, "layer table entry is 64 bytes");
 
 __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileElems - 1) >> kTileShift; }
-
-// Fused blockwise quantisation (+ int8 double quantisation when dq) and, when
-// err_partial != nullptr, in-register dequantisation and the fp64 squared
-// error, written as kPartsPerTile partials per tile to err_partial; with
-// sq_partial != nullptr too, also the sum of x^2, laid out the same way.
-// ragged: some layer's n is not a multiple of kTileElems (adds the tail launch).
-hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, int dtype,
-                        bool dq, double* err_partial, double* sq_partial, hipStream_t s);
-// Per-layer fixed-order sum of the per-tile partials into err[nl].
-hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
-                         hipStream_t s);
-// Standalone dequantisation (qabsmax/scale2 when dq, else absmax); desc_ws:
-// device scratch for one 32-byte record per tile (kPartsPerTile doubles).
-hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                          void* desc_ws, hipStream_t s);
-// Standalone double quantisation of absmax.
-hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s);
-// Budgeted top-K; rank/perm are int32[nl] workspace arrays.
-// Codec variants (block 32/64/128/256; second-level kind 0 none, 1 int8,
-// 2 int8 minus the mean absmax, 3 E4M3 minus the mean absmax).  The table's
-// tile_end counts groups of 256 blocks of the variant's block size.
-// gsum and partial: one fp64 per group.
-hipError_t launch_variant_error(const LayerDesc* tab, int nl, int64_t ngroups, int dtype, int block,
-                                int kind, float* mean, double* gsum, double* partial, double* err,
-                                hipStream_t s);
-// rec_ws: device scratch for one 64-byte record per group.
-hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups, int dtype,
-                                  int block, int kind, const float* mean, void* rec_ws, hipStream_t s);
-// NF4 weight dequantised into the matmul that consumes it (bf16 MFMA):
-// forward out[m x rows] = x[m x cols] * W^T, backward out[m x cols] =
-// x[m x rows] * W; W [rows x cols] given by its codes and constants
-// (qabsmax + scale2 when qabsmax != nullptr, else absmax).  rows and cols
-// multiples of 128; out fp32 or bf16.
-hipError_t launch_nf4_matmul(const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
-                             const float* absmax, int64_t rows, int64_t cols, bool forward,
-                             const void* x, int64_t m, void* out, bool out_f32, hipStream_t s);
-hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,
-                         int kcap, uint8_t* selected, int32_t* k_out, int32_t* rank,
-                         int32_t* perm, hipStream_t s);
-// Selection variants: unit = layer, or group of consecutive layers when
-// group_end (device, nu entries) is given; score = err (/ denom when given);
-// rule 0 = longest prefix within the budget, 1 = fill past what does not fit.
-struct SelectScratch {
-    int32_t* rank;    // [nu]
-    int32_t* perm;    // [nu]
-    double* uscore;   // [nu]
-    int64_t* ucost;   // [nu]
-    uint8_t* flag;    // [nu]
-};
-hipError_t launch_select_ex(const double* err, const double* denom, const int64_t* cost,
-                            const int32_t* group_end, int nu, int64_t budget, int kcap, int rule,
-                            uint8_t* selected, int32_t* k_out, SelectScratch w, hipStream_t s);
 
 }  // namespace nf4k
