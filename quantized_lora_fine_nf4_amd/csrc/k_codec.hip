@@ -1,14 +1,14 @@
 // k_codec.hip -- NF4 codec kernels for gfx950 (CDNA4, wave64).
 //
 // One tile = one double-quantisation group = 256 blocks of 64 weights
-// (16384 weights, 32 KB of bf16).  A 256-thread workgroup (4 waves) owns a
-// tile at a time; the tiles of all layers form one flat index, so one grouped
-// launch covers the whole stack (persistent workgroups walking the index for
-// the fused and double-quant kernels, one workgroup per tile for the
-// standalone dequantisation).  Lane layout: wave w, load j
-// (j = 0..7), lane L reads weights w*4096 + j*512 + 8L .. +8 with one 128-bit
-// load, so each load instruction of a wave covers 1 KB contiguously and the 8
-// lanes 8m..8m+7 hold the 64 weights of one block.
+// (16384 weights, 32 KB of bf16).  The tiles of all layers form one flat
+// index, so one grouped launch covers the whole stack.  The fused and
+// double-quant kernels are persistent: a 256-thread workgroup (4 waves) owns a
+// tile at a time; lane layout: wave w, load j (j = 0..7), lane L reads weights
+// w*4096 + j*512 + 8L .. +8 with one 128-bit load, so each load instruction of
+// a wave covers 1 KB contiguously and the 8 lanes 8m..8m+7 hold the 64 weights
+// of one block.  The standalone dequantisation is a one-shot grid of small
+// workgroups, each a quarter tile, reading a per-tile record (see there).
 //
 // What is computed (see nf4.h for the full format):
 //   absmax      -- "quantisation constants" per block ("QLoRA" paper summary
@@ -302,23 +302,6 @@ __device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_
     const int64_t rem = n - r.e0;
     r.valid = rem < kTileElems ? (int)rem : kTileElems;
     return r;
-}
-
-// Layer holding `tile` = the number of layers whose tile_end is <= tile
-// (tile_end grows with the layer index), found by one wave with two ballots:
-// lanes sample every s-th layer, then the s layers after the last sample that
-// ends at or before the tile.  Up to 4096 layers; beyond, the binary search.
-__device__ __forceinline__ int find_layer(const LayerDesc* tab, int nl, int64_t tile)
-{
-    if (nl > 4096) return first_layer(tab, nl, tile);
-    const int lane = threadIdx.x & 63;
-    const int s = (nl + 63) >> 6;
-    const int i = lane * s;
-    const int c = __popcll(__builtin_amdgcn_ballot_w64(i < nl && tab[i].tile_end <= tile));
-    if (s == 1 || c == 0) return c;
-    const int base = (c - 1) * s + 1;
-    const int j = base + lane;
-    return base + __popcll(__builtin_amdgcn_ballot_w64(lane < s && j < nl && tab[j].tile_end <= tile));
 }
 
 // ---- fused quantise / double-quantise / dequantise / error --------------
