@@ -30,7 +30,8 @@ def command(out: str = LIB_PATH) -> list:
 
 
 def cpu_command(out: str = CPU_LIB_PATH) -> list:
-    """The host-CPU pass (OpenMP, portable AVX2 target, no FMA contraction)."""
+    """The host-CPU pass (OpenMP, AVX2 baseline with an AVX-512 tile path chosen at run time,
+    no FMA contraction)."""
     return ["g++", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", "-shared", "-fopenmp",
             "-ffp-contract=off", "-fno-fast-math", "-Wall",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
