@@ -23,7 +23,9 @@ extern "C" {
  * equal the GPU pass's bit for bit; err is summed in fp64 (per 16384-weight
  * tile in element order, then the tiles in order).  threads <= 0: the OpenMP
  * default.  Synchronous.  NF4_E_ARG on NULL/size errors, NF4_E_UNSUPPORTED on
- * formats other than block 64 with dq_group 0 or 256, bf16 or fp16. */
+ * formats other than block 64 with dq_group 0 or 256, bf16 or fp16.  Uses an
+ * AVX-512 code path when the CPU has it (same outputs bit for bit); the
+ * environment variable NF4_CPU_ISA=avx2 selects the AVX2 path instead. */
 nf4_status nf4_cpu_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                                double* err, int32_t threads);
 

@@ -55,8 +55,12 @@ namespace avx512 {
 }  // namespace avx512
 #pragma GCC pop_options
 
-static bool have_avx512(void)
+// The AVX-512 path when the CPU has it, unless NF4_CPU_ISA=avx2 asks for the
+// portable one (read at every call; lets both paths be compared on one host).
+static bool use_avx512(void)
 {
+    const char* isa = getenv("NF4_CPU_ISA");
+    if (isa && strcmp(isa, "avx2") == 0) return false;
     __builtin_cpu_init();
     return __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
            __builtin_cpu_supports("avx512dq") && __builtin_cpu_supports("avx512vl") &&
@@ -91,7 +95,7 @@ nf4_status nf4_cpu_layer_error(const nf4_layer* layers, int32_t nl, nf4_format f
     double* part = (double*)malloc(sizeof(double) * (size_t)ntiles);
     if (!part) { free(first); return NF4_E_ARG; }
     init_tables();
-    const bool wide = have_avx512();
+    const bool wide = use_avx512();
     if (threads > 0) omp_set_num_threads(threads);
 #pragma omp parallel for schedule(dynamic, 8)
     for (int64_t t = 0; t < ntiles; ++t) {

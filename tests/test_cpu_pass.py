@@ -124,3 +124,31 @@ def test_cpu_library_exports_its_header():
     L = ctypes.CDLL(cpu.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_cpu_pass_isa_paths_agree_bitwise():
+    """The AVX-512 and AVX2 tile paths give the same bits (each run in its own
+    process, the path chosen with NF4_CPU_ISA)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys, numpy as np; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "import quantized_lora_fine_nf4_amd as q, synth\n"
+        "from quantized_lora_fine_nf4_amd import cpu\n"
+        "ws = [synth.generate_raw(950 + k, n, dtype=d) for k, (n, d) in enumerate("
+        "[(70_001, 0), (16384 * 3 + 5, 1), (333, 0)])]\n"
+        "outs = []\n"
+        "for dt in (0, 1):\n"
+        "    o = cpu.layer_error([w for w in ws], q.fmt(dt, True), threads=4)\n"
+        "    outs.append(np.concatenate([o['err'].view(np.uint8)] + o['codes'] + "
+        "[x.view(np.uint8) for x in o['qabsmax'] + o['scale2']]))\n"
+        "sys.stdout.write(np.concatenate(outs).tobytes().hex())\n"
+    ) % (ROOT, os.path.join(ROOT, "tests"))
+    res = {}
+    for isa in ("avx2", "auto"):
+        env = dict(os.environ, NF4_CPU_ISA=isa)
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        res[isa] = r.stdout
+    assert res["avx2"] == res["auto"] and len(res["avx2"]) > 1000
