@@ -108,18 +108,35 @@ def cpu_baseline(cfg, seconds: float, n_deq: int, n_total: int):
     slice_n = 64 * 16384
     done, t_fused, t_deq = 0, 0.0, 0.0
     i = 0
-    while t_fused + t_deq < seconds:
-        w = synth.generate(cfg, i % cfg.n_layers, first=0, count=min(slice_n, cfg.n(i % cfg.n_layers)))
-        t0 = time.perf_counter()
-        r = oracle.layer_error(w, cfg.dtype, cfg.dq)
-        t1 = time.perf_counter()
-        y = oracle.dequantize(r["codes"], w.size, cfg.dtype, qabsmax=r["qabsmax"], scale2=r["scale2"])
-        t2 = time.perf_counter()
-        assert np.array_equal(y, r["y"])
-        t_fused += t1 - t0
-        t_deq += t2 - t1
-        done += w.size
-        i += 1
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})         # the timed work on one core
+    try:
+        while t_fused + t_deq < seconds:
+            w = synth.generate(cfg, i % cfg.n_layers, first=0,
+                               count=min(slice_n, cfg.n(i % cfg.n_layers)), threads=1)
+            t0 = time.perf_counter()
+            r = oracle.layer_error(w, cfg.dtype, cfg.dq)
+            t1 = time.perf_counter()
+            consts = (dict(qabsmax=r["qabsmax"], scale2=r["scale2"]) if cfg.dq
+                      else dict(absmax=r["absmax"]))
+            y = oracle.dequantize(r["codes"], w.size, cfg.dtype, **consts)
+            t2 = time.perf_counter()
+            assert np.array_equal(y, r["y"])
+            t_fused += t1 - t0
+            t_deq += t2 - t1
+            done += w.size
+            i += 1
+    finally:
+        os.sched_setaffinity(0, allowed)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     per_w_fused = t_fused / done
     per_w_deq = t_deq / done
     step_s = per_w_fused * n_total + cfg.dequant_repeats * per_w_deq * n_deq
@@ -129,6 +146,8 @@ def cpu_baseline(cfg, seconds: float, n_deq: int, n_total: int):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
+        "cpu": {"model": model, "pinned_core": core, "cores_available": len(allowed),
+                "compiler": " ".join(oracle.BUILD_FLAGS)},
         "sample": (f"{done} weights ({i} slices of 64 double-quant groups, first slice of "
                    f"successive matrices): fused oracle pass {t_fused:.2f} s "
                    f"({2 * done / t_fused / 1e6:.1f} MB/s of bf16), oracle dequant "
@@ -197,6 +216,13 @@ def variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes, r
     t_norm = timed(lambda: q.nf4_layer_error_norm(ls, f, err, sq, ws))
     res["nf4_layer_error_ms"] = round(t_plain, 4)
     res["nf4_layer_error_norm_ms"] = round(t_norm, 4)
+    e, q2 = err.cpu().double(), sq.cpu().double()
+    n = torch.tensor([float(x) for x in cfg.sizes], dtype=torch.float64)
+    rel = e / q2
+    res["error_stats"] = {   # the GPU pass's own scores: SSE, MSE = SSE / n, relative = SSE / sum x^2
+        "sse_total": float(e.sum()), "mse_mean": float((e / n).mean()),
+        "relative_mean": float(rel.mean()), "relative_min": float(rel.min()),
+        "relative_max": float(rel.max())}
     res["nf4_layer_error_norm_GBps"] = round(fused_bytes / (t_norm * 1e-3) / 1e9, 1)
     m = len(cfg.per_block)
     ge = list(range(m, nl + 1, m))
@@ -476,10 +502,11 @@ def main():
         "nf4_layer_error": {"ms": round(fused_ms, 4),
                             "algorithmic_GB": round(fused_bytes / 1e9, 4),
                             "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1)},
-        "nf4_dequantize": {"ms": round(deq_ms, 4), "launches_per_step": cfg.dequant_repeats,
-                           "algorithmic_GB": round(deq_bytes / 1e9, 4),
-                           "GBps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1)},
     }
+    if cfg.dequant_repeats > 0:   # configurations without the dequantisation phase time the pass only
+        kernels["nf4_dequantize"] = {"ms": round(deq_ms, 4), "launches_per_step": cfg.dequant_repeats,
+                                     "algorithmic_GB": round(deq_bytes / 1e9, 4),
+                                     "GBps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1)}
     for k in kernels.values():
         k["frac_of_peak"] = round(k["GBps"] / HBM_PEAK_GBS, 4)
     # dominant kernel: the larger share of the step's time
@@ -515,8 +542,8 @@ def main():
     }
     if not args.no_variants:
         out["variants"] = variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes)
-        if cfg.dtype == q.NF4_BF16 and all(r % 128 == 0 and c % 128 == 0
-                                             for _, r, c in cfg.per_block):
+        if cfg.dtype == q.NF4_BF16 and cfg.dequant_repeats > 0 and all(
+                r % 128 == 0 and c % 128 == 0 for _, r, c in cfg.per_block):
             out["matmul"] = matmul_block(q, torch, ls, f, cfg, stream, deq_ms / max(1, n_deq),
                                          set(keep))
     if args.protocol > 0:

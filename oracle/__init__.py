@@ -24,10 +24,12 @@ BF16, FP16 = 0, 1
 BLOCK, DQ_GROUP = 64, 256
 
 
+BUILD_FLAGS = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math"]
+
+
 def build() -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp",
+    cmd = [*BUILD_FLAGS, "-fPIC", "-shared", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp",
            *SOURCES, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(LIB_PATH + ".tmp", LIB_PATH)
