@@ -242,18 +242,19 @@ nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_varia
  * forward and the backward pass ("QLoRA" paper summary page, How It Works);
  * AQLoRA names that as where quantised fine-tuning loses its time ("AQLoRA"
  * arXiv listing, English abstract).  The weight tile is dequantised into
- * on-chip memory, to exactly the bf16 values nf4_dequantize writes, and
+ * on-chip memory, to exactly the 16-bit values nf4_dequantize writes, and
  * multiplied there; the 16-bit weight never goes to memory.
  *   w        one matrix W [rows x cols] (w->n == rows * cols), row-major, in
  *            its NF4 form: codes, and qabsmax + scale2 (dq_group 256) or absmax
  *   backward 0: out[m x rows] = x[m x cols] * W^T   (forward, y = x W^T)
  *            1: out[m x cols] = x[m x rows] * W     (input gradient, dx = dy W)
- *   x        device bf16 [m x (cols | rows)], row-major, 16-byte aligned
+ *   x        device [m x (cols | rows)] in fmt.dtype (bf16 or fp16),
+ *            row-major, 16-byte aligned
  *   out      device [m x (rows | cols)], row-major, 16-byte aligned:
- *            fp32 (out_fp32 = 1) or bf16 rounded to nearest even (0)
- * Products of two bf16 values are exact in fp32; the sums are fp32 (matrix
- * core accumulation).  fmt.dtype must be NF4_BF16 and rows, cols multiples of
- * 128 (else NF4_E_UNSUPPORTED); 1 <= m < 2^31; codes 16-byte aligned.  No
+ *            fp32 (out_fp32 = 1) or fmt.dtype rounded to nearest even (0)
+ * Products of two bf16 or two fp16 values are exact in fp32; the sums are
+ * fp32 (matrix core accumulation).  rows, cols must be multiples of 128
+ * (else NF4_E_UNSUPPORTED); 1 <= m < 2^31; codes 16-byte aligned.  No
  * workspace; enqueues only.  Deterministic run to run. */
 nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                       int32_t backward, const void* x, int64_t m, void* out,

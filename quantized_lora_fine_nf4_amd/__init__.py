@@ -220,7 +220,7 @@ def nf4_matmul(layer, rows: int, cols: int, f: nf4_format, x, out, backward: boo
                stream=None) -> None:
     """out = x @ W^T (forward) or x @ W (backward) with W in NF4 form.
     layer: an nf4_layer struct (e.g. ls.c_layers[i]); x, out: device tensors
-    (out float32 or bfloat16)."""
+    (x in the 16-bit type f.dtype names; out float32 or that 16-bit type)."""
     import torch
     m = int(x.shape[0]) if x.dim() > 1 else 1
     out_fp32 = 1 if out.dtype == torch.float32 else 0

@@ -69,6 +69,7 @@ static_assert(kBN % 128 == 0 && kBM % 32 == 0, "tile shape");
 constexpr int kLdp = kBK + 8;     // LDS row pitch in 16-bit elements (144 B: conflict-free 16-B reads)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -79,11 +80,39 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Two fp32 values rounded to bf16 (nearest, ties to even), packed low first.
-__device__ __forceinline__ uint32_t pack_bf16(float y0, float y1)
+// Keeps a product from being fused with its conversion to fp16 (v_fma_mix*
+// rounds the exact product once; the format rounds to fp32 first).
+__device__ __forceinline__ float opaque(float x)
 {
-    f2 in = {y0, y1};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(in, bf2));
+    __asm__ volatile("" : "+v"(x));
+    return x;
+}
+
+// Two fp32 values rounded to the 16-bit type DT (0 bf16, 1 fp16; nearest,
+// ties to even), packed low first.
+template <int DT>
+__device__ __forceinline__ uint32_t pack16(float y0, float y1)
+{
+    if constexpr (DT == 0) {
+        f2 in = {y0, y1};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(in, bf2));
+    } else {
+        const _Float16 h0 = (_Float16)opaque(y0), h1 = (_Float16)opaque(y1);
+        return (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    }
+}
+
+// MFMA fragment of eight 16-bit values of type DT, and the 32x32x16 product.
+template <int DT> struct Frag8 { typedef bf16x8 T; };
+template <> struct Frag8<1> { typedef f16x8 T; };
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(const typename Frag8<DT>::T& a, const typename Frag8<DT>::T& b,
+                                         const f32x16& c)
+{
+    if constexpr (DT == 0) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 struct GemmArgs {
@@ -125,7 +154,8 @@ __device__ __forceinline__ float block_const(const RawConst& c)
 }
 
 // Eight codes (one dword, element 2j in the low nibble of byte j) to eight
-// bf16 values, packed in four dwords.
+// 16-bit values, packed in four dwords.
+template <int DT>
 __device__ __forceinline__ u32x4 deq8(uint32_t c, float adq, const float* lv)
 {
     u32x4 r;
@@ -135,12 +165,12 @@ __device__ __forceinline__ u32x4 deq8(uint32_t c, float adq, const float* lv)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const f2 p = lp[(c >> (8 * j)) & 255];
-        r[j] = pack_bf16(p.x * adq, p.y * adq);
+        r[j] = pack16<DT>(p.x * adq, p.y * adq);
     }
 #else
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        r[j] = pack_bf16(lv[(c >> (8 * j)) & 15] * adq, lv[(c >> (8 * j + 4)) & 15] * adq);
+        r[j] = pack16<DT>(lv[(c >> (8 * j)) & 15] * adq, lv[(c >> (8 * j + 4)) & 15] * adq);
 #endif
     return r;
 }
@@ -192,7 +222,7 @@ __device__ __forceinline__ void load_step(StepRegs& r, const GemmArgs& g, int64_
     }
 }
 
-template <bool FWD, bool DQ>
+template <int DT, bool FWD, bool DQ>
 __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint16_t* Ws,
                                            const float* lv)
 {
@@ -207,13 +237,13 @@ __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint
             uint16_t* dst = Ws + (128 * p + (t >> 1)) * kLdp + 32 * (t & 1);
             const float adq = block_const<DQ>(r.k[p][0]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *(u32x4*)(dst + 8 * j) = deq8(r.w[p][j], adq, lv);
+            for (int j = 0; j < 4; ++j) *(u32x4*)(dst + 8 * j) = deq8<DT>(r.w[p][j], adq, lv);
         } else {
             // transposed: Ws[k][n] with the reduction index n contiguous; this thread's
             // four rows n0..n0+3 are consecutive, so each column gets one 8-byte write
             u32x4 y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = deq8(r.w[p][i], block_const<DQ>(r.k[p][i]), lv);
+            for (int i = 0; i < 4; ++i) y[i] = deq8<DT>(r.w[p][i], block_const<DQ>(r.k[p][i]), lv);
             const int n0 = 4 * (t & 15), cc = 128 * p + 8 * (t >> 4);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -233,7 +263,7 @@ __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint
 #define NF4_GEMM_MIN_WG 3         // workgroups per CU the register allocation must allow
 #endif
 
-template <bool FWD, bool DQ, bool OUT_F32>
+template <int DT, bool FWD, bool DQ, bool OUT_F32>
 __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t s_a[NF4_GEMM_STAGES][kBM * kLdp];
@@ -283,7 +313,7 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
     StepRegs regs;
     load_step<FWD, DQ>(regs, g, m0, c0, 0);
     __syncthreads();   // level table
-    store_step<FWD, DQ>(regs, s_a[0], s_w[0], s_lv);
+    store_step<DT, FWD, DQ>(regs, s_a[0], s_w[0], s_lv);
     __syncthreads();
 
     for (int s = 0; s < nsteps; ++s) {
@@ -295,21 +325,22 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int kof = 16 * kk + 8 * (lane >> 5);
-            bf16x8 fa[kTM], fb[kTN];
+            typedef typename Frag8<DT>::T F;
+            F fa[kTM], fb[kTN];
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
-                fa[i] = *(const bf16x8*)(As + (kWM * wm + 32 * i + (lane & 31)) * kLdp + kof);
+                fa[i] = *(const F*)(As + (kWM * wm + 32 * i + (lane & 31)) * kLdp + kof);
 #pragma unroll
             for (int j = 0; j < kTN; ++j)
-                fb[j] = *(const bf16x8*)(Ws + (kWN * wn + 32 * j + (lane & 31)) * kLdp + kof);
+                fb[j] = *(const F*)(Ws + (kWN * wn + 32 * j + (lane & 31)) * kLdp + kof);
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
 #pragma unroll
                 for (int j = 0; j < kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma32<DT>(fa[i], fb[j], acc[i][j]);
         }
         if (NF4_GEMM_STAGES == 1) __syncthreads();   // every wave done reading the one buffer
-        if (more) store_step<FWD, DQ>(regs, s_a[cur ^ (NF4_GEMM_STAGES - 1)],
+        if (more) store_step<DT, FWD, DQ>(regs, s_a[cur ^ (NF4_GEMM_STAGES - 1)],
                                       s_w[cur ^ (NF4_GEMM_STAGES - 1)], s_lv);
         __syncthreads();
     }
@@ -329,7 +360,7 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
                         ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
                     else
                         ((GLOBAL uint16_t*)g.out)[row * g.ldo + col] =
-                            (uint16_t)pack_bf16(acc[i][j][r], 0.0f);
+                            (uint16_t)pack16<DT>(acc[i][j][r], 0.0f);
                 }
             }
 }
@@ -337,14 +368,14 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
 // One-shot launches of at most 2^32 / 256 - 1 workgroups each.
 constexpr int64_t kMaxGemmGrid = (int64_t(1) << 32) / kGThreads - 1;
 
-template <bool FWD, bool DQ, bool OUT_F32>
+template <int DT, bool FWD, bool DQ, bool OUT_F32>
 hipError_t gemm_go(GemmArgs g, hipStream_t s)
 {
     const int64_t ntiles = ((g.M + kBM - 1) / kBM) * g.ntn;
     for (int64_t t0 = 0; t0 < ntiles; t0 += kMaxGemmGrid) {
         const int64_t n = ntiles - t0 < kMaxGemmGrid ? ntiles - t0 : kMaxGemmGrid;
         g.tile0 = t0;
-        hipLaunchKernelGGL((k_nf4_matmul<FWD, DQ, OUT_F32>), dim3((unsigned)n), dim3(kGThreads), 0, s, g);
+        hipLaunchKernelGGL((k_nf4_matmul<DT, FWD, DQ, OUT_F32>), dim3((unsigned)n), dim3(kGThreads), 0, s, g);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -353,7 +384,7 @@ hipError_t gemm_go(GemmArgs g, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_nf4_matmul(const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
+hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
                              const float* absmax, int64_t rows, int64_t cols, bool forward,
                              const void* x, int64_t m, void* out, bool out_f32, hipStream_t s)
 {
@@ -373,14 +404,18 @@ hipError_t launch_nf4_matmul(const uint8_t* codes, const int8_t* qabsmax, const 
     g.ntn = g.ncol / kBN;
     g.tile0 = 0;
     const bool dq = qabsmax != nullptr;
-#define NF4_GEMM(F, D, O) return gemm_go<F, D, O>(g, s)
-    if (forward) {
-        if (dq) { if (out_f32) NF4_GEMM(true, true, true); else NF4_GEMM(true, true, false); }
-        else    { if (out_f32) NF4_GEMM(true, false, true); else NF4_GEMM(true, false, false); }
-    } else {
-        if (dq) { if (out_f32) NF4_GEMM(false, true, true); else NF4_GEMM(false, true, false); }
-        else    { if (out_f32) NF4_GEMM(false, false, true); else NF4_GEMM(false, false, false); }
+#define NF4_GEMM(T, F, D, O) return gemm_go<T, F, D, O>(g, s)
+#define NF4_GEMM_DT(T)                                                                             \
+    if (forward) {                                                                               \
+        if (dq) { if (out_f32) NF4_GEMM(T, true, true, true); else NF4_GEMM(T, true, true, false); }     \
+        else    { if (out_f32) NF4_GEMM(T, true, false, true); else NF4_GEMM(T, true, false, false); }   \
+    } else {                                                                                     \
+        if (dq) { if (out_f32) NF4_GEMM(T, false, true, true); else NF4_GEMM(T, false, true, false); }   \
+        else    { if (out_f32) NF4_GEMM(T, false, false, true); else NF4_GEMM(T, false, false, false); } \
     }
+    if (dtype == 0) { NF4_GEMM_DT(0) }
+    NF4_GEMM_DT(1)
+#undef NF4_GEMM_DT
 #undef NF4_GEMM
 }
 

@@ -392,7 +392,6 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
 {
     nf4_status st = check_format(fmt);
     if (st != NF4_OK) return st;
-    if (fmt.dtype != NF4_BF16) return NF4_E_UNSUPPORTED;
     if (!w || !x || !out) return NF4_E_ARG;
     if (rows <= 0 || cols <= 0 || m <= 0 || m >= (int64_t(1) << 31)) return NF4_E_ARG;
     if (rows > kMaxN / cols || w->n != rows * cols) return NF4_E_ARG;
@@ -403,7 +402,7 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
     if (!w->codes || (dq ? (!w->qabsmax || !w->scale2) : !w->absmax)) return NF4_E_ARG;
     if (!aligned(w->codes, 16) || !aligned(x, 16) || !aligned(out, 16)) return NF4_E_ALIGN;
     if (dq ? !aligned(w->scale2, 4) : !aligned(w->absmax, 4)) return NF4_E_ALIGN;
-    hipError_t e = nf4k::launch_nf4_matmul(w->codes, dq ? w->qabsmax : nullptr,
+    hipError_t e = nf4k::launch_nf4_matmul(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
                                            dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax,
                                            rows, cols, backward == 0, x, m, out, out_fp32 == 1,
                                            static_cast<hipStream_t>(stream));

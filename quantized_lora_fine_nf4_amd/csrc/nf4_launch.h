@@ -39,8 +39,9 @@ hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups,
 // forward out[m x rows] = x[m x cols] * W^T, backward out[m x cols] =
 // x[m x rows] * W; W [rows x cols] given by its codes and constants
 // (qabsmax + scale2 when qabsmax != nullptr, else absmax).  rows and cols
-// multiples of 128; out fp32 or bf16.
-hipError_t launch_nf4_matmul(const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
+// multiples of 128; x and the dequantised W in the 16-bit type dtype (0 bf16,
+// 1 fp16); out fp32 or that 16-bit type.
+hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
                              const float* absmax, int64_t rows, int64_t cols, bool forward,
                              const void* x, int64_t m, void* out, bool out_f32, hipStream_t s);
 hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,

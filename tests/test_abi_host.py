@@ -242,7 +242,8 @@ def test_matmul_arguments():
              backward=0, x=FAKE, m=10, out=FAKE, out_fp32=1):
         lay = q.nf4_layer(rows * cols if n is None else n, None, codes, absmax, qa, s2, None)
         return L.nf4_matmul(ctypes.byref(lay), rows, cols, fmt, backward, x, m, out, out_fp32, None)
-    assert call(fmt=q.fmt(q.NF4_FP16, True)) == q.NF4_E_UNSUPPORTED
+    assert call(fmt=q.nf4_format(2, 64, 256)) == q.NF4_E_UNSUPPORTED
+    assert call(fmt=q.fmt(q.NF4_FP16, True), m=0) == q.NF4_E_ARG       # fp16 accepted
     assert call(fmt=q.nf4_format(0, 32, 256)) == q.NF4_E_UNSUPPORTED
     assert call(rows=200, n=200 * cols) == q.NF4_E_UNSUPPORTED
     assert call(cols=100, n=rows * 100) == q.NF4_E_UNSUPPORTED

@@ -2,11 +2,12 @@
 
 The weight's NF4 form is made by the oracle on the host and uploaded, so the
 test isolates the matmul.  Reference: the oracle's dequantised weight and an
-fp64 product.  Bound (fp32 accumulation of exact bf16 products over K terms):
-|out - ref| <= 2 K 2^-24 (|x| |W|^T) elementwise.  The bf16 output equals the
-round-to-nearest-even of the same kernel's fp32 output.  Ragged m (1, 77,
-300), several tile counts, double quant on and off, forward and backward;
-the 14B stack's FFN shape (13824 x 5120) at m = 4096 on sampled rows.
+fp64 product.  Bound (fp32 accumulation of exact bf16 or fp16 products over K
+terms): |out - ref| <= 2 K 2^-24 (|x| |W|^T) elementwise.  The 16-bit output
+equals the round-to-nearest-even of the same kernel's fp32 output.  bf16 and
+fp16, ragged m (1, 77, 300), several tile counts, double quant on and off,
+forward and backward; the 14B stack's FFN shape (13824 x 5120) at m = 4096
+on sampled rows.
 """
 import numpy as np
 import pytest
@@ -18,7 +19,8 @@ import synth
 from conftest import print_case
 
 pytestmark = pytest.mark.gpu
-BF16 = q.NF4_BF16
+BF16, FP16 = q.NF4_BF16, q.NF4_FP16
+TORCH16 = {BF16: torch.bfloat16, FP16: torch.float16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,9 +34,9 @@ def _device():
 class DevWeight:
     """A matrix's NF4 form (from the oracle) in device memory."""
 
-    def __init__(self, rows, cols, seed, dq, outliers=0.0):
-        w = synth.generate_raw(seed, rows * cols, dtype=BF16, outlier_frac=outliers)
-        codes, absmax = oracle.quantize(w, BF16)
+    def __init__(self, rows, cols, seed, dq, outliers=0.0, dtype=BF16):
+        w = synth.generate_raw(seed, rows * cols, dtype=dtype, outlier_frac=outliers)
+        codes, absmax = oracle.quantize(w, dtype)
         self.consts = dict(absmax=absmax)
         self.codes = torch.from_numpy(codes).cuda()
         self.absmax = torch.from_numpy(absmax).cuda()
@@ -45,34 +47,34 @@ class DevWeight:
             self.q = torch.from_numpy(qa).cuda()
             self.s2 = torch.from_numpy(s2).cuda()
         self.np_codes = codes
-        self.rows, self.cols, self.dq = rows, cols, dq
+        self.rows, self.cols, self.dq, self.dtype = rows, cols, dq, dtype
         ptr = lambda t: None if t is None else int(t.data_ptr())
         self.layer = q.nf4_layer(rows * cols, None, ptr(self.codes),
                                  None if dq else ptr(self.absmax), ptr(self.q), ptr(self.s2), None)
 
     def dense(self):
-        y = oracle.dequantize(self.np_codes, self.rows * self.cols, BF16, **self.consts)
-        return oracle.from16(y, BF16).astype(np.float64).reshape(self.rows, self.cols)
+        y = oracle.dequantize(self.np_codes, self.rows * self.cols, self.dtype, **self.consts)
+        return oracle.from16(y, self.dtype).astype(np.float64).reshape(self.rows, self.cols)
 
 
-def _x(m, k, seed):
+def _x(m, k, seed, dtype=BF16):
     rng = np.random.default_rng(seed)
-    return oracle.to16_rne(rng.standard_normal(m * k).astype(np.float32), BF16).reshape(m, k)
+    return oracle.to16_rne(rng.standard_normal(m * k).astype(np.float32), dtype).reshape(m, k)
 
 
 def _run(W, xb, backward, out_f32=True):
     m = xb.shape[0]
     ncol = W.cols if backward else W.rows
     x = torch.from_numpy(xb.view(np.int16)).cuda()
-    out = torch.full((m, ncol), float("nan"), dtype=torch.float32 if out_f32 else torch.bfloat16,
+    out = torch.full((m, ncol), float("nan"), dtype=torch.float32 if out_f32 else TORCH16[W.dtype],
                      device="cuda")
-    q.nf4_matmul(W.layer, W.rows, W.cols, q.fmt(BF16, W.dq), x, out, backward=backward)
+    q.nf4_matmul(W.layer, W.rows, W.cols, q.fmt(W.dtype, W.dq), x, out, backward=backward)
     torch.cuda.synchronize()
     return out
 
 
 def _check(out, xb, W, backward, rows_idx=None):
-    x = oracle.from16(xb, BF16).astype(np.float64).reshape(xb.shape)
+    x = oracle.from16(xb, W.dtype).astype(np.float64).reshape(xb.shape)
     if rows_idx is not None:
         x = x[rows_idx]
     Wd = W.dense()
@@ -94,16 +96,17 @@ def _check(out, xb, W, backward, rows_idx=None):
 @pytest.mark.parametrize("dq", [False, True], ids=["nodq", "dq"])
 @pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 256)], ids=lambda s: f"{s[0]}x{s[1]}")
 @pytest.mark.parametrize("m", [1, 77, 128, 300])
-def test_matmul_matches_oracle(m, shape, dq, backward):
+@pytest.mark.parametrize("dtype", [BF16, FP16], ids=["bf16", "fp16"])
+def test_matmul_matches_oracle(dtype, m, shape, dq, backward):
     rows, cols = shape
-    print_case("nf4_matmul", m, rows, cols, "dq" if dq else "nodq", "bwd" if backward else "fwd")
-    W = DevWeight(rows, cols, 7000 + rows + cols, dq, outliers=0.002)
-    xb = _x(m, rows if backward else cols, 11 * m + rows)
+    print_case("nf4_matmul", dtype, m, rows, cols, "dq" if dq else "nodq", "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 7000 + rows + cols, dq, outliers=0.002, dtype=dtype)
+    xb = _x(m, rows if backward else cols, 11 * m + rows, dtype)
     out = _run(W, xb, backward)
     _check(out, xb, W, backward)
-    # bf16 output: RNE of the same fp32 sums
+    # 16-bit output: RNE of the same fp32 sums
     o16 = _run(W, xb, backward, out_f32=False)
-    assert torch.equal(o16, out.to(torch.bfloat16))
+    assert torch.equal(o16, out.to(TORCH16[dtype]))
 
 
 def test_matmul_is_deterministic():
@@ -115,12 +118,13 @@ def test_matmul_is_deterministic():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
-def test_matmul_fullsize_ffn_sampled(backward):
+@pytest.mark.parametrize("backward,dtype", [(False, BF16), (True, BF16), (False, FP16)],
+                         ids=["fwd-bf16", "bwd-bf16", "fwd-fp16"])
+def test_matmul_fullsize_ffn_sampled(backward, dtype):
     rows, cols, m = 13824, 5120, 4096
-    print_case("nf4_matmul full size", rows, cols, m, "bwd" if backward else "fwd")
-    W = DevWeight(rows, cols, 99, True, outliers=0.0005)
-    xb = _x(m, rows if backward else cols, 100)
+    print_case("nf4_matmul full size", dtype, rows, cols, m, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 99, True, outliers=0.0005, dtype=dtype)
+    xb = _x(m, rows if backward else cols, 100, dtype)
     out = _run(W, xb, backward)
     rng = np.random.default_rng(5)
     idx = np.sort(np.r_[0, m - 1, rng.integers(0, m, 6)])
