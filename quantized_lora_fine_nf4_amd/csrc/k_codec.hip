@@ -50,7 +50,7 @@ constexpr int kYStride = NF4_YSTRIDE;  // per-block dequant table, code-major, p
 #define NF4_CODEC_WAVES_PER_EU 4     // schedule the fused loop for 128 VGPRs (measured fastest)
 #endif
 #ifndef NF4_CODEC_WG_PER_CU
-#define NF4_CODEC_WG_PER_CU 3        // resident fused workgroups per CU (3 measured faster than 2 or 4)
+#define NF4_CODEC_WG_PER_CU 4        // resident fused workgroups per CU (4 measured faster than 2 or 3)
 #endif
 #ifndef NF4_SCHED_FENCE
 #define NF4_SCHED_FENCE 1            // scheduling fence every 8 (1) or 4 (2) weights in the fused kernel
@@ -257,8 +257,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 
 // ---- tile walk ---------------------------------------------------------
 
+// A tile's place in its matrix, with the matrix's buffers.  The buffers are
+// read from the layer table when the tile is chosen, with a wave-uniform
+// layer index, so they are scalar loads; read later, inside the tile's
+// processing, they were vector loads queued behind the next tile's weight
+// loads, and waiting for them drained that prefetch.
 struct TileRef {
-    const LayerDesc* d;
+    const void* w;
+    uint8_t* codes;
+    float* absmax;
+    int8_t* qabsmax;
+    float* scale2;
     int64_t local;   // tile index within the layer
     int64_t e0;      // first element of the tile within the layer
     int valid;       // elements of the tile inside the layer (1..16384)
@@ -294,13 +303,51 @@ __device__ __forceinline__ int first_layer(const LayerDesc* tab, int nl, int64_t
 __device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_t tile)
 {
     while (tab[l].tile_end <= tile) ++l;
+    l = __builtin_amdgcn_readfirstlane(l);
+    const LayerDesc& d = tab[l];
     TileRef r;
-    r.d = &tab[l];
-    const int64_t n = r.d->n;
-    r.local = tile - (r.d->tile_end - tiles_of(n));
+    r.w = d.w;
+    r.codes = d.codes;
+    r.absmax = d.absmax;
+    r.qabsmax = d.qabsmax;
+    r.scale2 = d.scale2;
+    const int64_t n = d.n;
+    r.local = tile - (d.tile_end - tiles_of(n));
     r.e0 = r.local << kTileShift;
     const int64_t rem = n - r.e0;
     r.valid = rem < kTileElems ? (int)rem : kTileElems;
+    return r;
+}
+
+// The fused kernel's walk counts tiles in 32 bits (its launcher rejects 2^31
+// tiles or more): wave-uniform 32-bit compares are scalar instructions, while
+// 64-bit signed compares need vector registers, which the loop holds for good.
+__device__ __forceinline__ int first_layer32(const LayerDesc* tab, int nl, int tile)
+{
+    int lo = 0, hi = nl - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)tab[mid].tile_end > tile) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ TileRef tile_ref32(const LayerDesc* tab, int& l, int tile)
+{
+    while ((int)tab[l].tile_end <= tile) ++l;
+    l = __builtin_amdgcn_readfirstlane(l);
+    const LayerDesc& d = tab[l];
+    TileRef r;
+    r.w = d.w;
+    r.codes = d.codes;
+    r.absmax = d.absmax;
+    r.qabsmax = d.qabsmax;
+    r.scale2 = d.scale2;
+    const int64_t n = d.n;
+    r.local = tile - ((int)d.tile_end - (int)tiles_of(n));
+    r.e0 = r.local << kTileShift;
+    const int64_t rem = n - r.e0;   // >= 1
+    r.valid = (rem >> kTileShift) != 0 ? kTileElems : (int)rem;
     return r;
 }
 
@@ -336,6 +383,17 @@ struct CodecShared {
 // high nibble) and whose bytes past the end are not written.
 // NORM (with ERR): also the sum of x^2 over the lane's weights, in the same
 // precision and with the same 2^k scaling as the error.
+// 16-bit view of LDS words written as halves and read whole
+typedef uint16_t __attribute__((may_alias)) u16_alias;
+
+// Per-launch LDS set-up of the fused kernels: the encode cells, and the bf16
+// dequant table's lower halves (zero; the tiles write only the upper halves).
+__device__ void init_shared(CodecShared& sh)
+{
+    build_cells(sh.cells);
+    for (int i = threadIdx.x; i < 16 * kYStride; i += kCThreads) sh.ytab[i] = 0.0f;
+}
+
 struct LaneSums {
     double err;
     double sq;
@@ -348,12 +406,16 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
     const int lane = threadIdx.x & 63;
     const EncCell* cells = sh.cells + (lane & (kRepl - 1));
     const uint32_t lb = lane_base<kCThreads>();
+    // load j covers elements lb + 512 j ..: block (lb >> 6) + 8 j, code bytes
+    // (lb >> 1) + 256 j; written as base + constant so that the constants
+    // become immediate offsets of the memory instructions
+    const uint32_t b0 = lb >> 6, c0 = lb >> 1;
     float e = 0.0f, q = 0.0f;
     double acc64 = 0.0, sq64 = 0.0;
 #pragma unroll
     for (int j = 0; j < kCLoads; ++j) {
         const uint32_t o = lb + j * 512u;
-        const int bidx = (int)(o >> 6);
+        const int bidx = (int)(b0 + 8u * j);
         const float r64 = sh.r64[bidx];
         float scale = 1.0f;
         int ek = 0;
@@ -397,7 +459,7 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
             }
         }
         if constexpr (FULL) {
-            *(g_u32)(cp + (o >> 1)) = pk;
+            *(g_u32)(cp + (c0 + 256u * j)) = pk;
         } else {
             const int rem = valid - (int)o;
             if (rem >= 8) {
@@ -435,7 +497,7 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
 template <bool FULL>
 __device__ __forceinline__ void load_tile(u32x4 (&v)[kCLoads], const TileRef& tr)
 {
-    const g_cu16 w = (g_cu16)tr.d->w + tr.e0;
+    const g_cu16 w = (g_cu16)tr.w + tr.e0;
     const int valid = tr.valid;
     const uint32_t lb = lane_base<kCThreads>();
     if constexpr (FULL) {
@@ -468,18 +530,19 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
                                               double* __restrict__ partial,
                                               double* __restrict__ partial_sq)
 {
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const LayerDesc& d = *tr.d;
+    // the wave index as a scalar (wave-uniform): no vector register held for it
+    const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const TileRef& d = tr;
     const int valid = tr.valid;
 
     // 2. block absmax (exact: a max of representable values), and the wave's
     //    largest for the double-quant group maximum
-    const uint32_t lb = lane_base<kCThreads>();
+    const uint32_t b0 = lane_base<kCThreads>() >> 6;   // block of load j: b0 + 8 j
     uint32_t wm = 0;
 #pragma unroll
     for (int j = 0; j < kCLoads; ++j) {
         const uint32_t m = max8_u32(absmax_bits8(v[j]));
-        if ((lane & 7) == 0) sh.amax[(lb + j * 512u) >> 6] = m;
+        if ((lane & 7) == 0) sh.amax[b0 + 8u * j] = m;
         wm = max(wm, m);
     }
     if constexpr (DQ) {
@@ -524,14 +587,23 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
     sh.pre[t] = pre;
     sh.escale[t] = ek;
     if constexpr (ERR) {
-        // the block's 16 dequantised values, rounded to the 16-bit type, back in fp32
+        // the block's 16 dequantised values, rounded to the 16-bit type, back in
+        // fp32.  A bf16 value is the upper half of its fp32 pattern, so for bf16
+        // only the upper halves are written (the lower halves stay zero from
+        // init_shared) and no conversion back is needed.
 #pragma unroll
         for (int c = 0; c < 16; c += 2) {
             float y0, y1;
-            (void)round_pair<DT>(as_f(nf4fmt::kLevelBits[c]) * adq,
-                                 as_f(nf4fmt::kLevelBits[c + 1]) * adq, y0, y1);
-            sh.ytab[c * kYStride + t] = y0;
-            sh.ytab[(c + 1) * kYStride + t] = y1;
+            const uint32_t p = round_pair<DT>(as_f(nf4fmt::kLevelBits[c]) * adq,
+                                              as_f(nf4fmt::kLevelBits[c + 1]) * adq, y0, y1);
+            if constexpr (DT == 0) {
+                u16_alias* yt = reinterpret_cast<u16_alias*>(sh.ytab);
+                yt[2 * (c * kYStride + t) + 1] = (uint16_t)p;
+                yt[2 * ((c + 1) * kYStride + t) + 1] = (uint16_t)(p >> 16);
+            } else {
+                sh.ytab[c * kYStride + t] = y0;
+                sh.ytab[(c + 1) * kYStride + t] = y1;
+            }
         }
     }
     {
@@ -580,20 +652,21 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
     double* __restrict__ partial_sq)
 {
     __shared__ CodecShared sh;
-    build_cells(sh.cells);
+    init_shared(sh);
     __syncthreads();
-    int64_t tile = walk_start<false>();
-    if (tile >= ntiles) return;
-    int l = first_layer(tab, nl, tile);
-    TileRef tr0 = tile_ref(tab, l, tile), tr1;
+    const int nt = (int)ntiles;
+    int tile = (int)walk_start<false>();
+    if (tile >= nt) return;
+    int l = first_layer32(tab, nl, tile);
+    TileRef tr0 = tile_ref32(tab, l, tile), tr1;
     u32x4 v0[kCLoads], v1[kCLoads];
     int par = 0;
     if (tr0.valid == kTileElems) load_tile<true>(v0, tr0);
     for (;;) {
-        int64_t nxt = tile + gridDim.x;
-        bool more = nxt < ntiles;
+        int nxt = tile + (int)gridDim.x;
+        bool more = nxt < nt;
         if (more) {
-            tr1 = tile_ref(tab, l, nxt);
+            tr1 = tile_ref32(tab, l, nxt);
             if (tr1.valid == kTileElems) load_tile<true>(v1, tr1);
         }
         if (tr0.valid == kTileElems) {
@@ -602,10 +675,10 @@ __global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
         }
         if (!more) break;
         tile = nxt;
-        nxt = tile + gridDim.x;
-        more = nxt < ntiles;
+        nxt = tile + (int)gridDim.x;
+        more = nxt < nt;
         if (more) {
-            tr0 = tile_ref(tab, l, nxt);
+            tr0 = tile_ref32(tab, l, nxt);
             if (tr0.valid == kTileElems) load_tile<true>(v0, tr0);
         }
         if (tr1.valid == kTileElems) {
@@ -627,7 +700,7 @@ __global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __res
     const int64_t n = tab[blockIdx.x].n;
     if ((n & (kTileElems - 1)) == 0) return;
     __shared__ CodecShared sh;
-    build_cells(sh.cells);
+    init_shared(sh);
     __syncthreads();
     int l = blockIdx.x;
     const int64_t tile = tab[l].tile_end - 1;
@@ -815,7 +888,7 @@ __global__ __launch_bounds__(kThreads) void k_double_quant(const LayerDesc* __re
     int l = first_layer(tab, nl, start);
     for (int64_t tile = start; tile < ntiles; tile += gridDim.x) {
         const TileRef tr = tile_ref(tab, l, tile);
-        const LayerDesc& d = *tr.d;
+        const TileRef& d = tr;
         const int nbv = (tr.valid + 63) >> 6;
         const int64_t b = (tr.e0 >> 6) + t;
         const float a = (t < nbv) ? ((g_cf32)d.absmax)[b] : 0.0f;
@@ -890,6 +963,7 @@ hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, d
                     double* partial_sq, hipStream_t s)
 {
     auto k = k_codec<DT, DQ, ERR, NORM>;
+    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // the walk counts in 32 bits
     const int64_t grid = persistent_grid(k, ntiles, kCThreads, NF4_CODEC_WG_PER_CU);
     hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kCThreads), 0, s, tab, nl, ntiles, partial,
                        partial_sq);
