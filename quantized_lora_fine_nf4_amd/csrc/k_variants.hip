@@ -391,7 +391,14 @@ __global__ __launch_bounds__(64) void k_var_mean(const LayerDesc* __restrict__ t
 // Encode load j's 8 weights, store their codes, return their squared errors
 // (the same fp64 difference per weight as the definition; past the end of the
 // matrix x = 0 and y = +-0, which adds nothing).
-template <int DT, int B, bool FULL, bool SPEC>
+// D32: the difference is taken in fp32, where it is exact for kinds 0 and 1:
+// y is 0 (difference x), or y has the sign of x and a' lies within a factor
+// 2 of a (kind 0: a' = a; kind 1 with q >= 1: a in [s2/2, 3 s2/2] for q = 1 and
+// |a' - a| <= s2/2 above), and every nonzero code has |x| >= 0.03 a, so the two
+// 16-bit values are within 2^8 of each other in magnitude and their difference
+// fits in 24 bits.  Kinds 2 and 3 give no such bound (a small block's a' comes
+// from the matrix mean) and keep the fp64 difference.
+template <int DT, int B, bool FULL, bool SPEC, bool D32>
 __device__ __forceinline__ double encode_load(const VShared& sh, const u32x4 v, int j, const VGroup& g,
                                               GLOBAL uint8_t* cp)
 {
@@ -414,7 +421,8 @@ __device__ __forceinline__ double encode_load(const VShared& sh, const u32x4 v, 
             const float u = (SPEC ? x[h] * pre : x[h]) * r64;
             const VCell c = cells[((int)u + 64) * kVRepl];
             const uint32_t code = c.base + (u > c.thr ? 1u : 0u);
-            const double dd = (double)x[h] - (double)yt[__umul24(code, (uint32_t)kVYs)];
+            const float y = yt[__umul24(code, (uint32_t)kVYs)];
+            const double dd = D32 ? (double)(x[h] - y) : (double)x[h] - (double)y;
             acc = __builtin_fma(dd, dd, acc);
             pk |= code << (8 * k2 + 4 * h);
         }
@@ -440,7 +448,7 @@ struct Held {
     u32x4 v[(B <= NF4_VAR_HOLD) ? B / 8 : 1];
 };
 
-template <int DT, int B, bool FULL, bool SPEC, bool HOLD>
+template <int DT, int B, bool FULL, bool SPEC, bool HOLD, bool D32>
 __device__ __forceinline__ double encode_group(const VShared& sh, const Held<B>& held,
                                                const GLOBAL uint16_t* w, const VGroup& g,
                                                GLOBAL uint8_t* cp)
@@ -449,7 +457,7 @@ __device__ __forceinline__ double encode_group(const VShared& sh, const Held<B>&
     double acc = 0.0;
     if constexpr (HOLD) {
 #pragma unroll
-        for (int j = 0; j < NL; ++j) acc += encode_load<DT, B, FULL, SPEC>(sh, held.v[j], j, g, cp);
+        for (int j = 0; j < NL; ++j) acc += encode_load<DT, B, FULL, SPEC, D32>(sh, held.v[j], j, g, cp);
     } else {
         // last loads first: for the kinds that read the group a second time,
         // what the absmax pass loaded last is the likeliest still in cache
@@ -461,7 +469,7 @@ __device__ __forceinline__ double encode_group(const VShared& sh, const Held<B>&
 #pragma unroll
             for (int i = 0; i < BATCH; ++i) v[i] = vload<FULL>(w, voff<B>(j0 + i), g.valid);
 #pragma unroll
-            for (int i = 0; i < BATCH; ++i) acc += encode_load<DT, B, FULL, SPEC>(sh, v[i], j0 + i, g, cp);
+            for (int i = 0; i < BATCH; ++i) acc += encode_load<DT, B, FULL, SPEC, D32>(sh, v[i], j0 + i, g, cp);
         }
     }
     return acc;
@@ -546,8 +554,9 @@ __device__ __forceinline__ void var_codec_body(VShared& sh, const VGroup& g, int
     const bool spec = __syncthreads_or(pre != 1.0f);
 
     // 4. encode, store codes, squared error
-    const double acc = spec ? encode_group<DT, B, FULL, true, HOLD>(sh, held, w, g, cp)
-                            : encode_group<DT, B, FULL, false, HOLD>(sh, held, w, g, cp);
+    constexpr bool D32 = KIND <= 1;
+    const double acc = spec ? encode_group<DT, B, FULL, true, HOLD, D32>(sh, held, w, g, cp)
+                            : encode_group<DT, B, FULL, false, HOLD, D32>(sh, held, w, g, cp);
 
     // 5. the group's fp64 partial (waves in order)
     const double ws = wave_sum(acc);
