@@ -20,6 +20,9 @@ thread_local int32_t g_last_hip = 0;
 
 constexpr int64_t kMaxN = int64_t(1) << 40;
 constexpr int32_t kMaxLayers = 1 << 24;
+// tiles of 16,384 weights over all matrices of one call: the fused kernel's
+// persistent walk counts them in 32 bits (2^31 tiles are 3.5e13 weights)
+constexpr int64_t kMaxTiles = int64_t(1) << 31;
 constexpr int32_t kMaxSelectLayers = 65536;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -59,6 +62,7 @@ nf4_status check_layers(const nf4_layer* L, int32_t nl, unsigned need, int64_t* 
         if ((need & NEED_OUT) && !aligned(x.out, 16)) return NF4_E_ALIGN;
         ntiles += nf4k::tiles_of(x.n);
     }
+    if (ntiles >= kMaxTiles) return NF4_E_UNSUPPORTED;
     *ntiles_out = ntiles;
     return NF4_OK;
 }
@@ -253,6 +257,7 @@ size_t nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format f)
         if (n_per_layer[i] <= 0 || n_per_layer[i] >= kMaxN) return 0;
         ntiles += nf4k::tiles_of(n_per_layer[i]);
     }
+    if (ntiles >= kMaxTiles) return 0;
     return table_bytes(nl) + 2 * partial_bytes(ntiles);   // error and sum-of-squares partials
 }
 

@@ -117,6 +117,19 @@ def test_bad_layers(name):
 
 
 @pytest.mark.parametrize("name", CODEC)
+def test_tile_count_limit(name):
+    """At most 2^31 - 1 tiles of 16,384 weights per call: 64 matrices of 2^39
+    weights are 2^31 tiles (checked before anything is enqueued, so fake
+    pointers suffice); one tile fewer passes the size checks."""
+    f = q.fmt()
+    big = [_L(n=1 << 39) for _ in range(64)]
+    assert _call(name, big, f) == q.NF4_E_UNSUPPORTED
+    assert q.nf4_workspace_bytes([1 << 39] * 64, f) == 0
+    fits = [1 << 39] * 63 + [(1 << 39) - (1 << 14)]
+    assert q.nf4_workspace_bytes(fits, f) > 0
+
+
+@pytest.mark.parametrize("name", CODEC)
 def test_misaligned_pointers(name):
     f = q.fmt()
     fields = {"nf4_quantize": {"w": 16, "codes": 4, "absmax": 4, "scale2": 4},
