@@ -49,6 +49,9 @@ constexpr int kYStride = NF4_YSTRIDE;  // per-block dequant table, code-major, p
 #ifndef NF4_CODEC_WAVES_PER_EU
 #define NF4_CODEC_WAVES_PER_EU 4     // schedule the fused loop for 128 VGPRs (measured fastest)
 #endif
+#ifndef NF4_QUANT_WAVES_PER_EU
+#define NF4_QUANT_WAVES_PER_EU 3     // the loop without the error (nf4_quantize): 4 spilled, 3 does not
+#endif
 #ifndef NF4_CODEC_WG_PER_CU
 #define NF4_CODEC_WG_PER_CU 4        // resident fused workgroups per CU (4 measured faster than 2 or 3)
 #endif
@@ -647,7 +650,7 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 // buffer parity advances per processed tile: between two uses of one parity
 // the workgroup passes a barrier.
 template <int DT, bool DQ, bool ERR, bool NORM>
-__global__ __launch_bounds__(kCThreads, NF4_CODEC_WAVES_PER_EU) void k_codec(
+__global__ __launch_bounds__(kCThreads, ERR ? NF4_CODEC_WAVES_PER_EU : NF4_QUANT_WAVES_PER_EU) void k_codec(
     const LayerDesc* __restrict__ tab, int nl, int64_t ntiles, double* __restrict__ partial,
     double* __restrict__ partial_sq)
 {
