@@ -26,6 +26,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GB/s of bf16 weights through NF4 quant+dequant+error; % of HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+# VALU issue peak: 256 CUs x 4 SIMDs, one wave64 vector instruction per SIMD every
+# 4 cycles (16 lanes wide) at 2.4 GHz = 614.4 G wave-instructions/s
+VALU_PEAK_GIPS = 256 * 4 * 2.4 / 4
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -57,21 +60,39 @@ def codec_source_hash() -> str:
     return source_hash(CODEC_SOURCES)
 
 
-def read_traffic(workload_key: str, kernel: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current sources of the codec kernels (else None)."""
-    path = os.path.join(PROFILES, f"traffic_{workload_key}.txt")
+def read_profile_value(name: str, key: str):
+    """A value from a committed counter summary (`key=value` lines), if the
+    summary was taken on the current sources of the codec kernels (else None)."""
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
-        if "=" in line and not line.startswith("#"):
+        if "=" in line and not line.startswith("#") and not line.startswith(" "):
             k, v = line.strip().split("=", 1)
             vals[k.strip()] = v.strip()
     if vals.get("codec_source_hash") != codec_source_hash():
         return None
-    v = vals.get(f"{kernel}_bytes_per_launch")
+    v = vals.get(key)
     return float(v) if v else None
+
+
+def read_traffic(workload_key: str, kernel: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary."""
+    return read_profile_value(f"traffic_{workload_key}.txt", f"{kernel}_bytes_per_launch")
+
+
+def alu_roofline(workload_key: str, kernel: str, weights: int, ms: float):
+    """The kernel against the VALU issue peak: vector instructions per weight
+    from the committed SQ_INSTS_VALU summary (same sources only), times the
+    weights of one launch, over the launch time measured here."""
+    vpw = read_profile_value(f"counters_{workload_key}.txt", f"{kernel}_valu_per_weight")
+    if vpw is None:
+        return None
+    gips = vpw * weights / 64 / (ms * 1e-3) / 1e9
+    return {"bound": "alu", "valu_per_weight": vpw, "achieved": round(gips, 1),
+            "peak": VALU_PEAK_GIPS, "unit": "G wave64 VALU instructions/s",
+            "frac": round(gips / VALU_PEAK_GIPS, 4)}
 
 
 def cpu_pass(cfg, n_total: int, blocks: int = 1):
@@ -509,6 +530,11 @@ def main():
                                      "GBps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1)}
     for k in kernels.values():
         k["frac_of_peak"] = round(k["GBps"] / HBM_PEAK_GBS, 4)
+    kernels["nf4_layer_error"]["alu"] = alu_roofline(args.config, "nf4_layer_error", n_total, fused_ms)
+    if "nf4_dequantize" in kernels:
+        kernels["nf4_dequantize"]["alu"] = alu_roofline(args.config, "nf4_dequantize", n_deq, deq_ms)
+    for name, k in kernels.items():
+        k["traffic"] = read_traffic(args.config, name)
     # dominant kernel: the larger share of the step's time
     dom = "nf4_dequantize" if cfg.dequant_repeats * deq_ms > fused_ms else "nf4_layer_error"
     dk = kernels[dom]
