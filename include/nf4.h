@@ -113,9 +113,9 @@ typedef struct {
 
 /* One weight matrix ("layer"), flattened row-major, n elements, nb = ceil(n/64)
  * blocks, ng = ceil(nb/256) groups.  Which fields a call reads or writes is
- * listed at each call; unused fields may be NULL.  The codec calls take at
- * most 2^31 - 1 tiles of 16,384 weights in total (sum of ceil(n/16384) over
- * the matrices of one call), else NF4_E_UNSUPPORTED. */
+ * listed at each call; unused fields may be NULL.  The codec calls take
+ * fewer than 2^31 - 2^20 tiles of 16,384 weights in total (sum of
+ * ceil(n/16384) over the matrices of one call), else NF4_E_UNSUPPORTED. */
 typedef struct {
     int64_t     n;        /* elements, 1 <= n < 2^40                                   */
     const void* w;        /* device [n] 16-bit weights, 16-byte aligned                */

@@ -966,7 +966,8 @@ hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, d
                     double* partial_sq, hipStream_t s)
 {
     auto k = k_codec<DT, DQ, ERR, NORM>;
-    if (ntiles >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // the walk counts in 32 bits
+    // the walk counts in 32 bits: tile index + grid size must stay below 2^31
+    if (ntiles >= (int64_t(1) << 31) - (int64_t(1) << 20)) return hipErrorInvalidValue;
     const int64_t grid = persistent_grid(k, ntiles, kCThreads, NF4_CODEC_WG_PER_CU);
     hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kCThreads), 0, s, tab, nl, ntiles, partial,
                        partial_sq);

@@ -21,8 +21,9 @@ thread_local int32_t g_last_hip = 0;
 constexpr int64_t kMaxN = int64_t(1) << 40;
 constexpr int32_t kMaxLayers = 1 << 24;
 // tiles of 16,384 weights over all matrices of one call: the fused kernel's
-// persistent walk counts them in 32 bits (2^31 tiles are 3.5e13 weights)
-constexpr int64_t kMaxTiles = int64_t(1) << 31;
+// persistent walk counts them in 32 bits, tile index plus grid size included
+// (2^31 tiles are 3.5e13 weights)
+constexpr int64_t kMaxTiles = (int64_t(1) << 31) - (int64_t(1) << 20);
 constexpr int32_t kMaxSelectLayers = 65536;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -118,15 +118,21 @@ def test_bad_layers(name):
 
 @pytest.mark.parametrize("name", CODEC)
 def test_tile_count_limit(name):
-    """At most 2^31 - 1 tiles of 16,384 weights per call: 64 matrices of 2^39
-    weights are 2^31 tiles (checked before anything is enqueued, so fake
-    pointers suffice); one tile fewer passes the size checks."""
+    """Fewer than 2^31 - 2^20 tiles of 16,384 weights per call (checked before
+    anything is enqueued, so fake pointers suffice): 64 matrices of 2^39
+    weights are 2^31 tiles; exactly at the limit is refused, one tile below
+    it passes the size checks."""
     f = q.fmt()
     big = [_L(n=1 << 39) for _ in range(64)]
     assert _call(name, big, f) == q.NF4_E_UNSUPPORTED
     assert q.nf4_workspace_bytes([1 << 39] * 64, f) == 0
-    fits = [1 << 39] * 63 + [(1 << 39) - (1 << 14)]
-    assert q.nf4_workspace_bytes(fits, f) > 0
+    limit = (1 << 31) - (1 << 20)                       # tiles
+    at = [1 << 39] * 63 + [(limit - 63 * (1 << 25)) << 14]
+    assert sum(n >> 14 for n in at) == limit
+    assert _call(name, [_L(n=n) for n in at], f) == q.NF4_E_UNSUPPORTED
+    assert q.nf4_workspace_bytes(at, f) == 0
+    below = at[:-1] + [at[-1] - (1 << 14)]
+    assert q.nf4_workspace_bytes(below, f) > 0
 
 
 @pytest.mark.parametrize("name", CODEC)
