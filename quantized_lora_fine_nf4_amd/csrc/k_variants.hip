@@ -257,23 +257,36 @@ struct VGroup {
     int nbv;         // blocks of the group inside the matrix
 };
 
-template <int B>
-__device__ __forceinline__ VGroup vgroup(const LayerDesc* tab, int nl, int64_t g)
+// The matrix holding group g (binary search over the running group ends).
+__device__ __forceinline__ int group_layer(const LayerDesc* tab, int nl, int64_t g)
 {
     int lo = 0, hi = nl - 1;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (tab[mid].tile_end > g) hi = mid; else lo = mid + 1;
     }
+    return lo;
+}
+
+// Group g of matrix l.
+template <int B>
+__device__ __forceinline__ VGroup vgroup_of(const LayerDesc* tab, int l, int64_t g)
+{
     VGroup r;
-    r.d = &tab[lo];
-    r.l = lo;
-    r.local = g - (lo ? tab[lo - 1].tile_end : 0);
+    r.d = &tab[l];
+    r.l = l;
+    r.local = g - (l ? tab[l - 1].tile_end : 0);
     r.e0 = r.local * (int64_t)(kVThreads * B);
     const int64_t rem = r.d->n - r.e0;
     r.valid = rem < kVThreads * B ? (int)rem : kVThreads * B;
     r.nbv = (r.valid + B - 1) / B;
     return r;
+}
+
+template <int B>
+__device__ __forceinline__ VGroup vgroup(const LayerDesc* tab, int nl, int64_t g)
+{
+    return vgroup_of<B>(tab, group_layer(tab, nl, g), g);
 }
 
 // The thread index behind an opaque barrier: offsets derived from it are
@@ -578,8 +591,13 @@ __global__ __launch_bounds__(kVThreads, 4) void k_var_codec(const LayerDesc* __r
     __shared__ VShared sh;
     build_vcells(sh.cells);
     __syncthreads();
+    // the walk's groups only increase, so their matrix is found by stepping
+    // forward from the previous one: one table read per group where a binary
+    // search per group would chain about log2(matrices) dependent reads
+    int l = blockIdx.x < ngroups ? group_layer(tab, nl, blockIdx.x) : 0;
     for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
-        const VGroup g = vgroup<B>(tab, nl, gi);
+        while (tab[l].tile_end <= gi) ++l;
+        const VGroup g = vgroup_of<B>(tab, l, gi);
         if (g.valid == kVThreads * B) var_codec_body<DT, B, KIND, true>(sh, g, gi, mean, partial);
         else var_codec_body<DT, B, KIND, false>(sh, g, gi, mean, partial);
     }
