@@ -51,7 +51,7 @@ def lib() -> ctypes.CDLL:
 
 
 def default_threads() -> int:
-    # the GPU machine grants 16 CPUs per GPU whatever os.cpu_count() reports
+    # at most 16 threads: a GPU host may give a process 16 CPUs whatever os.cpu_count() reports
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
