@@ -303,17 +303,23 @@ __device__ __forceinline__ int first_layer(const LayerDesc* tab, int nl, int64_t
     return lo;
 }
 
-__device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_t tile)
+__device__ __forceinline__ TileRef buffers_of(const LayerDesc& d)
 {
-    while (tab[l].tile_end <= tile) ++l;
-    l = __builtin_amdgcn_readfirstlane(l);
-    const LayerDesc& d = tab[l];
     TileRef r;
     r.w = d.w;
     r.codes = d.codes;
     r.absmax = d.absmax;
     r.qabsmax = d.qabsmax;
     r.scale2 = d.scale2;
+    return r;
+}
+
+__device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_t tile)
+{
+    while (tab[l].tile_end <= tile) ++l;
+    l = __builtin_amdgcn_readfirstlane(l);
+    const LayerDesc& d = tab[l];
+    TileRef r = buffers_of(d);
     const int64_t n = d.n;
     r.local = tile - (d.tile_end - tiles_of(n));
     r.e0 = r.local << kTileShift;
@@ -322,9 +328,10 @@ __device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_
     return r;
 }
 
-// The fused kernel's walk counts tiles in 32 bits (its launcher rejects 2^31
-// tiles or more): wave-uniform 32-bit compares are scalar instructions, while
-// 64-bit signed compares need vector registers, which the loop holds for good.
+// The fused kernel's walk counts tiles in 32 bits (the entry points reject
+// 2^31 - 2^20 tiles or more): wave-uniform 32-bit compares are scalar
+// instructions, while 64-bit signed compares need vector registers, which the
+// loop holds for good.
 __device__ __forceinline__ int first_layer32(const LayerDesc* tab, int nl, int tile)
 {
     int lo = 0, hi = nl - 1;
@@ -340,12 +347,7 @@ __device__ __forceinline__ TileRef tile_ref32(const LayerDesc* tab, int& l, int 
     while ((int)tab[l].tile_end <= tile) ++l;
     l = __builtin_amdgcn_readfirstlane(l);
     const LayerDesc& d = tab[l];
-    TileRef r;
-    r.w = d.w;
-    r.codes = d.codes;
-    r.absmax = d.absmax;
-    r.qabsmax = d.qabsmax;
-    r.scale2 = d.scale2;
+    TileRef r = buffers_of(d);
     const int64_t n = d.n;
     r.local = tile - ((int)d.tile_end - (int)tiles_of(n));
     r.e0 = r.local << kTileShift;
@@ -372,6 +374,17 @@ struct CodecShared {
     uint32_t wmax[2][kCWaves];  // per tile parity, per wave: largest absmax bits of the wave's blocks
 };
 
+// 16-bit view of LDS words written as halves and read whole
+typedef uint16_t __attribute__((may_alias)) u16_alias;
+
+// Per-launch LDS set-up of the fused kernels: the encode cells, and the bf16
+// dequant table's lower halves (zero; the tiles write only the upper halves).
+__device__ void init_shared(CodecShared& sh)
+{
+    build_cells(sh.cells);
+    for (int i = threadIdx.x; i < 16 * kYStride; i += kCThreads) sh.ytab[i] = 0.0f;
+}
+
 // Step 4 of a tile for one lane: encode, pack and store the codes of its 64
 // weights; with ERR also look up each weight's dequantised value in the
 // block's table and add up the squared differences in fp32 over the lane's 64
@@ -386,17 +399,6 @@ struct CodecShared {
 // high nibble) and whose bytes past the end are not written.
 // NORM (with ERR): also the sum of x^2 over the lane's weights, in the same
 // precision and with the same 2^k scaling as the error.
-// 16-bit view of LDS words written as halves and read whole
-typedef uint16_t __attribute__((may_alias)) u16_alias;
-
-// Per-launch LDS set-up of the fused kernels: the encode cells, and the bf16
-// dequant table's lower halves (zero; the tiles write only the upper halves).
-__device__ void init_shared(CodecShared& sh)
-{
-    build_cells(sh.cells);
-    for (int i = threadIdx.x; i < 16 * kYStride; i += kCThreads) sh.ytab[i] = 0.0f;
-}
-
 struct LaneSums {
     double err;
     double sq;
