@@ -59,7 +59,7 @@ constexpr int kYStride = NF4_YSTRIDE;  // per-block dequant table, code-major, p
 #define NF4_SCHED_FENCE 1            // scheduling fence every 8 (1) or 4 (2) weights in the fused kernel
 #endif
 #ifndef NF4_NT_STORES
-#define NF4_NT_STORES 0              // non-temporal 128-bit stores of dequantised output
+#define NF4_NT_STORES 1              // non-temporal stores of codes and dequantised output (write-once streams)
 #endif
 #ifndef NF4_XCD_WALK
 #define NF4_XCD_WALK 1               // XCD-contiguous tile order within each pass of a persistent walk
@@ -86,6 +86,20 @@ typedef GLOBAL uint16_t* g_u16;
 typedef GLOBAL u32x4* g_u4;
 typedef GLOBAL int8_t* g_i8;
 typedef GLOBAL float* g_f32;
+
+// Stores of streams written once and not read back by the same kernel (codes,
+// dequantised weights): non-temporal, so they do not displace cached lines
+// (measured: dequantisation 5.03 -> 4.87 ms, fused pass 6.79 -> 6.74 ms on the
+// 14B stack).
+template <typename T>
+__device__ __forceinline__ void store_stream(const T& v, GLOBAL T* p)
+{
+#if NF4_NT_STORES
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -464,7 +478,7 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
             }
         }
         if constexpr (FULL) {
-            *(g_u32)(cp + (c0 + 256u * j)) = pk;
+            store_stream(pk, (g_u32)(cp + (c0 + 256u * j)));
         } else {
             const int rem = valid - (int)o;
             if (rem >= 8) {
@@ -729,15 +743,6 @@ constexpr int kDqElems = kTileElems / kDqSplit;       // weights per workgroup
 constexpr int kDqSteps = kDqElems / (kDqThreads * 8); // 16-byte stores per thread
 static_assert(kDqSteps >= 1 && kDqSteps * kDqThreads * 8 * kDqSplit == kTileElems, "dequant split");
 
-template <typename T>
-__device__ __forceinline__ void store16(GLOBAL T* p, const T& v)
-{
-#if NF4_NT_STORES
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
-}
 
 // Per-tile descriptor, built by k_dq_prep in the workspace before the
 // dequantisation: everything a workgroup needs about its tile in one 32-byte
@@ -848,7 +853,7 @@ __device__ __forceinline__ void dequant_unit(const float* s_lv, const DqTile& r,
         }
         if (full) {
             u32x4 pv = {p[0], p[1], p[2], p[3]};
-            store16((g_u4)(outp + o), pv);
+            store_stream(pv, (g_u4)(outp + o));
         } else {
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)

@@ -441,7 +441,7 @@ __device__ __forceinline__ double encode_load(const VShared& sh, const u32x4 v, 
         }
     }
     if (FULL || (int)o + 8 <= g.valid) {
-        *(GLOBAL uint32_t*)(cp + (o >> 1)) = pk;
+        __builtin_nontemporal_store(pk, (GLOBAL uint32_t*)(cp + (o >> 1)));   // write-once codes
     } else {
         const int rem = g.valid - (int)o;
         if (rem > 0) {
@@ -703,7 +703,8 @@ __global__ __launch_bounds__(kVdThreads) void k_var_dequant(const VarDqRec* __re
         for (int k2 = 0; k2 < 4; ++k2)
             p[k2] = round_pair<DT>(lv[(cw[j] >> (8 * k2)) & 15] * adq, lv[(cw[j] >> (8 * k2 + 4)) & 15] * adq);
         if (full || (int)o + 8 <= valid) {
-            *(GLOBAL u32x4*)(out + o) = u32x4{p[0], p[1], p[2], p[3]};
+            // write-once stream: non-temporal (4-7% faster than cached stores here)
+            __builtin_nontemporal_store(u32x4{p[0], p[1], p[2], p[3]}, (GLOBAL u32x4*)(out + o));
         } else {
             for (int k = 0; k < 8; ++k)
                 if ((int)o + k < valid) out[o + k] = (uint16_t)(p[k >> 1] >> (16 * (k & 1)));
