@@ -61,6 +61,9 @@ constexpr int kYStride = NF4_YSTRIDE;  // per-block dequant table, code-major, p
 #ifndef NF4_NT_STORES
 #define NF4_NT_STORES 1              // non-temporal stores of codes and dequantised output (write-once streams)
 #endif
+#ifndef NF4_NT_LOADS
+#define NF4_NT_LOADS 1               // non-temporal weight loads in the fused pass (read-once stream)
+#endif
 #ifndef NF4_XCD_WALK
 #define NF4_XCD_WALK 1               // XCD-contiguous tile order within each pass of a persistent walk
 #endif
@@ -98,6 +101,18 @@ __device__ __forceinline__ void store_stream(const T& v, GLOBAL T* p)
     __builtin_nontemporal_store(v, p);
 #else
     *p = v;
+#endif
+}
+
+// The fused pass reads each weight once: non-temporal loads (6.86 -> 6.74 ms
+// on the 14B stack).  The dequantisation's code loads measured slower so.
+template <typename T>
+__device__ __forceinline__ T load_stream(const GLOBAL T* p)
+{
+#if NF4_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
 #endif
 }
 
@@ -521,7 +536,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&v)[kCLoads], const TileRef& tr
     const uint32_t lb = lane_base<kCThreads>();
     if constexpr (FULL) {
 #pragma unroll
-        for (int j = 0; j < kCLoads; ++j) v[j] = *(g_cu4)(w + (lb + j * 512u));
+        for (int j = 0; j < kCLoads; ++j) v[j] = load_stream((g_cu4)(w + (lb + j * 512u)));
     } else {
 #pragma unroll
         for (int j = 0; j < kCLoads; ++j) {

@@ -315,11 +315,16 @@ __device__ __forceinline__ int vblock(int j)
     return (t >> 6) * 64 + j * (512 / B) + (t & 63) / (B / 8);
 }
 
-// 8 weights at group offset o; past the end of the matrix they read as 0
-template <bool FULL>
+// 8 weights at group offset o; past the end of the matrix they read as 0.
+// ONCE: the group is read only here (held in registers), so the load is
+// non-temporal; groups read twice keep their lines cached.
+template <bool FULL, bool ONCE = false>
 __device__ __forceinline__ u32x4 vload(const GLOBAL uint16_t* w, uint32_t o, int valid)
 {
-    if (FULL || (int)o + 8 <= valid) return *(const GLOBAL u32x4*)(w + o);
+    if (FULL || (int)o + 8 <= valid) {
+        if constexpr (ONCE) return __builtin_nontemporal_load((const GLOBAL u32x4*)(w + o));
+        else return *(const GLOBAL u32x4*)(w + o);
+    }
     uint32_t h[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) h[k] = ((int)o + k < valid) ? (uint32_t)w[o + k] : 0u;
@@ -506,7 +511,7 @@ __device__ __forceinline__ void var_codec_body(VShared& sh, const VGroup& g, int
     if constexpr (FUSED) {
         if constexpr (HOLD) {
 #pragma unroll
-            for (int j = 0; j < NL; ++j) held.v[j] = vload<FULL>(w, voff<B>(j), g.valid);
+            for (int j = 0; j < NL; ++j) held.v[j] = vload<FULL, true>(w, voff<B>(j), g.valid);
 #pragma unroll
             for (int j = 0; j < NL; ++j) absmax_of_load<DT, B>(held.v[j], j, g, sh.a);
         } else {
