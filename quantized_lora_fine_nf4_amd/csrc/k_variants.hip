@@ -316,8 +316,9 @@ __device__ __forceinline__ int vblock(int j)
 }
 
 // 8 weights at group offset o; past the end of the matrix they read as 0.
-// ONCE: the group is read only here (held in registers), so the load is
-// non-temporal; groups read twice keep their lines cached.
+// ONCE: the last read of these weights (a group held in registers, or the
+// encode's re-read), so the load is non-temporal; a first read that is read
+// again keeps its lines cached.
 template <bool FULL, bool ONCE = false>
 __device__ __forceinline__ u32x4 vload(const GLOBAL uint16_t* w, uint32_t o, int valid)
 {
@@ -485,7 +486,7 @@ __device__ __forceinline__ double encode_group(const VShared& sh, const Held<B>&
         for (int j0 = NL - BATCH; j0 >= 0; j0 -= BATCH) {
             u32x4 v[BATCH];
 #pragma unroll
-            for (int i = 0; i < BATCH; ++i) v[i] = vload<FULL>(w, voff<B>(j0 + i), g.valid);
+            for (int i = 0; i < BATCH; ++i) v[i] = vload<FULL, true>(w, voff<B>(j0 + i), g.valid);
 #pragma unroll
             for (int i = 0; i < BATCH; ++i) acc += encode_load<DT, B, FULL, SPEC, D32>(sh, v[i], j0 + i, g, cp);
         }
