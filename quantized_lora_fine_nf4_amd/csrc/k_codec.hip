@@ -8,7 +8,7 @@
 // w*4096 + j*512 + 8L .. +8 with one 128-bit load, so each load instruction of
 // a wave covers 1 KB contiguously and the 8 lanes 8m..8m+7 hold the 64 weights
 // of one block.  The standalone dequantisation is a one-shot grid of small
-// workgroups, each a quarter tile, reading a per-tile record (see there).
+// workgroups, each an eighth of a tile, reading a per-tile record (see there).
 //
 // What is computed (see nf4.h for the full format):
 //   absmax      -- "quantisation constants" per block ("QLoRA" paper summary
@@ -747,11 +747,11 @@ __global__ __launch_bounds__(kCThreads) void k_codec_tail(const LayerDesc* __res
 // ---- standalone dequantisation -------------------------------------------
 
 #ifndef NF4_DEQ_SPLIT
-#define NF4_DEQ_SPLIT 4              // workgroups per tile in the standalone dequantisation
+#define NF4_DEQ_SPLIT 8              // workgroups per tile in the standalone dequantisation
 #endif
 constexpr int kDqSplit = NF4_DEQ_SPLIT;
 #ifndef NF4_DEQ_THREADS
-#define NF4_DEQ_THREADS 128          // threads per dequantisation workgroup
+#define NF4_DEQ_THREADS 64           // threads per dequantisation workgroup (4 stores each)
 #endif
 constexpr int kDqThreads = NF4_DEQ_THREADS;
 constexpr int kDqElems = kTileElems / kDqSplit;       // weights per workgroup
@@ -809,7 +809,9 @@ __global__ __launch_bounds__(kThreads) void k_dq_prep(const LayerDesc* __restric
 // quarter tiles (4 stores per thread) 5.07 ms, half 5.99, whole 6.00; 64
 // threads: eighth tiles (4 stores) 5.07, quarter 5.97, sixteenth 5.67; 512
 // threads: half 5.41, quarter 7.70; an XCD-contiguous unit order changed
-// nothing.  What made the small workgroups pay off at all was issuing every
+// nothing.  With non-temporal output stores: 64 threads over eighth tiles
+// 4.855 ms, 128 over quarters 4.885, 128 over eighths 5.29, 256 over halves
+// 5.36, 128 over halves 5.96.  What made the small workgroups pay off at all was issuing every
 // load of a whole unit at once: with the constant load behind a bounds guard
 // each load was waited for in its own branch, and quarter tiles took 7.2 ms.
 template <int DT, bool DQ>
