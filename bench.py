@@ -367,6 +367,27 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
                      "achieved": tf(t_fwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tf(t_fwd) / MFMA_BF16_PEAK_TFS, 4)},
     }
+    # few tokens: the split-reduction path against dequantise + library GEMM
+    small = {}
+    for ms in (16, 128):
+        xs = torch.randn(ms, cols, dtype=torch.bfloat16, device="cuda", generator=gen)
+        gs = torch.randn(ms, rows, dtype=torch.bfloat16, device="cuda", generator=gen)
+        ysf = torch.empty(ms, rows, dtype=torch.bfloat16, device="cuda")
+        ysb = torch.empty(ms, cols, dtype=torch.bfloat16, device="cuda")
+        nf = q.nf4_matmul_workspace_bytes(rows, cols, False, ms)
+        nb = q.nf4_matmul_workspace_bytes(rows, cols, True, ms)
+        wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device="cuda") if nf else None
+        wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda") if nb else None
+        tf_ = timed(lambda: q.nf4_matmul_ws(layer, rows, cols, f, xs.view(torch.int16), ysf, wsf))
+        tb_ = timed(lambda: q.nf4_matmul_ws(layer, rows, cols, f, gs.view(torch.int16), ysb, wsb,
+                                            backward=True))
+        lf = timed(lambda: torch.matmul(xs, wt))
+        lb = timed(lambda: torch.matmul(gs, w))
+        small[f"m{ms}"] = {"fused_split_fwd_ms": round(tf_, 4), "fused_split_bwd_ms": round(tb_, 4),
+                           "dequant_then_library_fwd_ms": round(t_deq + lf, 4),
+                           "dequant_then_library_bwd_ms": round(t_deq + lb, 4)}
+        del xs, gs, ysf, ysb, wsf, wsb
+    res["small_m"] = small
     del x, gy, yf, yb, wt
     return res
 

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NF4_ABI_VERSION 2
+#define NF4_ABI_VERSION 3
 
 typedef enum {
     NF4_OK = 0,
@@ -262,7 +262,27 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
                       int32_t backward, const void* x, int64_t m, void* out,
                       int32_t out_fp32, void* stream);
 
+/* nf4_matmul with a caller workspace, for shapes whose output tiles alone do
+ * not fill the GPU (few tokens m): the reduction is then split into up to 16
+ * parts, each workgroup multiplies one output tile over one part into fp32
+ * partials in ws, and a second kernel adds the parts in part order (fixed, so
+ * the result is deterministic run to run) and rounds as nf4_matmul does.  The
+ * split count is a function of (rows, cols, backward, m) only.  Same
+ * arguments and results as nf4_matmul except the summation order; ws: device,
+ * 256-byte aligned, at least nf4_matmul_workspace_bytes(rows, cols, backward,
+ * m) bytes (NF4_E_WORKSPACE otherwise); when that is 0 the call is
+ * nf4_matmul and ws may be NULL.  Error bound as for nf4_matmul:
+ * (K/parts + parts) fp32 additions per output instead of K. */
+nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
+                         int32_t backward, const void* x, int64_t m, void* out,
+                         int32_t out_fp32, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- host-only helpers (pure; no HIP calls) ---- */
+
+/* Workspace of nf4_matmul_ws for this shape: parts * m * (rows | cols) fp32
+ * partials rounded up to 256 bytes, or 0 when the shape is not split (its
+ * output tiles fill the GPU) or on bad input. */
+size_t      nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m);
 
 /* Workspace for every codec call above over these matrices (the descriptor
  * table plus two arrays of 4 fp64 partials per 16384-weight tile); 0 on bad

@@ -87,6 +87,12 @@ EXPORTS = {
     "nf4_matmul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, nf4_format,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "nf4_matmul_ws": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, nf4_format,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]),
+    "nf4_matmul_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                     ctypes.c_int64]),
     "nf4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32, nf4_format]),
     "nf4_layer_error_variant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_variant,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -226,6 +232,23 @@ def nf4_matmul(layer, rows: int, cols: int, f: nf4_format, x, out, backward: boo
     out_fp32 = 1 if out.dtype == torch.float32 else 0
     _check(lib().nf4_matmul(ctypes.byref(layer), int(rows), int(cols), f, int(bool(backward)),
                             _ptr(x), m, _ptr(out), out_fp32, _stream(stream)), "nf4_matmul")
+
+
+def nf4_matmul_workspace_bytes(rows: int, cols: int, backward: bool, m: int) -> int:
+    return int(lib().nf4_matmul_workspace_bytes(int(rows), int(cols), int(bool(backward)), int(m)))
+
+
+def nf4_matmul_ws(layer, rows: int, cols: int, f: nf4_format, x, out, ws, backward: bool = False,
+                  stream=None) -> None:
+    """nf4_matmul with a workspace (ws: device uint8 tensor or None) for the
+    split-reduction path of small m."""
+    import torch
+    m = int(x.shape[0]) if x.dim() > 1 else 1
+    out_fp32 = 1 if out.dtype == torch.float32 else 0
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().nf4_matmul_ws(ctypes.byref(layer), int(rows), int(cols), f, int(bool(backward)),
+                               _ptr(x), m, _ptr(out), out_fp32, _ptr(ws), nbytes, _stream(stream)),
+           "nf4_matmul_ws")
 
 
 def variant(dtype: int = NF4_BF16, block: int = BLOCK, kind: int = NF4_DQ_INT8) -> nf4_variant:

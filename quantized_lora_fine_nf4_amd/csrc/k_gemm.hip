@@ -127,7 +127,11 @@ struct GemmArgs {
     int64_t ldo;
     int64_t M, kred, ncol;
     int64_t ntn;            // output column tiles
-    int64_t tile0;          // first tile of this launch
+    int64_t tile0;          // first (tile, split) index of this launch
+    int64_t ntiles;         // output tiles (row tiles x column tiles)
+    int nsplit;             // splits of the reduction (1: none)
+    int split_steps;        // k-steps per split
+    float* part;            // nsplit > 1: fp32 partials [nsplit][M x ncol]
 };
 
 // Raw constant of W block b as loaded: the int8 and its group scale with
@@ -263,7 +267,10 @@ __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint
 #define NF4_GEMM_MIN_WG 3         // workgroups per CU the register allocation must allow
 #endif
 
-template <int DT, bool FWD, bool DQ, bool OUT_F32>
+// PART: this workgroup sums one split of the reduction and stores it as an
+// fp32 partial (k_splitk_sum adds the splits in order); otherwise the whole
+// reduction, stored as fp32 or the 16-bit type.
+template <int DT, bool FWD, bool DQ, bool OUT_F32, bool PART>
 __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint16_t s_a[NF4_GEMM_STAGES][kBM * kLdp];
@@ -284,6 +291,9 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
     int64_t tile = g.tile0 + blockIdx.x;
     if (NF4_GEMM_XCD && (gridDim.x & 7) == 0)
         tile = g.tile0 + (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    // splits are the outer index: each split covers every output tile
+    const int split = PART ? (int)(tile / g.ntiles) : 0;
+    if (PART) tile -= (int64_t)split * g.ntiles;
     int64_t mt, nt;
     if (NF4_GEMM_GROUP_M > 0) {
         const int64_t per = (int64_t)NF4_GEMM_GROUP_M * g.ntn;
@@ -300,7 +310,10 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
     const int64_t m0 = mt * kBM;
     const int64_t c0 = nt * kBN;
     const int wm = wv >> 1, wn = wv & 1;   // this wave's kWM x kWN quarter
-    const int nsteps = (int)(g.kred / kBK);
+    const int ksteps = (int)(g.kred / kBK);
+    const int step0 = PART ? split * g.split_steps : 0;
+    const int nsteps = PART ? min(g.split_steps, ksteps - step0) : ksteps;
+    const int64_t kb = (int64_t)step0 * kBK;   // first reduction index of this split
 
     f32x16 acc[kTM][kTN];
 #pragma unroll
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     StepRegs regs;
-    load_step<FWD, DQ>(regs, g, m0, c0, 0);
+    load_step<FWD, DQ>(regs, g, m0, c0, kb);
     __syncthreads();   // level table
     store_step<DT, FWD, DQ>(regs, s_a[0], s_w[0], s_lv);
     __syncthreads();
@@ -319,7 +332,7 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
     for (int s = 0; s < nsteps; ++s) {
         const int cur = NF4_GEMM_STAGES == 2 ? (s & 1) : 0;
         const bool more = s + 1 < nsteps;
-        if (more) load_step<FWD, DQ>(regs, g, m0, c0, (int64_t)(s + 1) * kBK);
+        if (more) load_step<FWD, DQ>(regs, g, m0, c0, kb + (int64_t)(s + 1) * kBK);
         const uint16_t* As = s_a[cur];
         const uint16_t* Ws = s_w[cur];
 #pragma unroll
@@ -356,7 +369,9 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
                 const int64_t row = m0 + kWM * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 const int64_t col = c0 + kWN * wn + 32 * j + (lane & 31);
                 if (row < g.M) {
-                    if constexpr (OUT_F32)
+                    if constexpr (PART)
+                        ((GLOBAL float*)g.part)[(int64_t)split * g.M * g.ldo + row * g.ldo + col] = acc[i][j][r];
+                    else if constexpr (OUT_F32)
                         ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
                     else
                         ((GLOBAL uint16_t*)g.out)[row * g.ldo + col] =
@@ -365,28 +380,83 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
             }
 }
 
+// The fp32 partials of the splits added in split order (fixed, so the result
+// does not depend on timing), stored as fp32 or rounded to the 16-bit type.
+// Four outputs per thread; n is a multiple of 4 (ncol is a multiple of 128).
+template <int DT, bool OUT_F32>
+__global__ __launch_bounds__(256) void k_splitk_sum(const float* __restrict__ part, int nsplit,
+                                                    int64_t n, void* __restrict__ out)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    f4 acc = *(const GLOBAL f4*)(part + i);
+    for (int sp = 1; sp < nsplit; ++sp) acc += *(const GLOBAL f4*)(part + (int64_t)sp * n + i);
+    if constexpr (OUT_F32) {
+        *(GLOBAL f4*)((float*)out + i) = acc;
+    } else {
+        const u32x2 v = {pack16<DT>(acc.x, acc.y), pack16<DT>(acc.z, acc.w)};
+        *(GLOBAL u32x2*)((uint16_t*)out + i) = v;
+    }
+}
+
 // One-shot launches of at most 2^32 / 256 - 1 workgroups each.
 constexpr int64_t kMaxGemmGrid = (int64_t(1) << 32) / kGThreads - 1;
 
 template <int DT, bool FWD, bool DQ, bool OUT_F32>
 hipError_t gemm_go(GemmArgs g, hipStream_t s)
 {
-    const int64_t ntiles = ((g.M + kBM - 1) / kBM) * g.ntn;
-    for (int64_t t0 = 0; t0 < ntiles; t0 += kMaxGemmGrid) {
-        const int64_t n = ntiles - t0 < kMaxGemmGrid ? ntiles - t0 : kMaxGemmGrid;
+    const int64_t total = g.ntiles * g.nsplit;
+    for (int64_t t0 = 0; t0 < total; t0 += kMaxGemmGrid) {
+        const int64_t n = total - t0 < kMaxGemmGrid ? total - t0 : kMaxGemmGrid;
         g.tile0 = t0;
-        hipLaunchKernelGGL((k_nf4_matmul<DT, FWD, DQ, OUT_F32>), dim3((unsigned)n), dim3(kGThreads), 0, s, g);
+        if (g.nsplit > 1)
+            hipLaunchKernelGGL((k_nf4_matmul<DT, FWD, DQ, OUT_F32, true>), dim3((unsigned)n), dim3(kGThreads),
+                               0, s, g);
+        else
+            hipLaunchKernelGGL((k_nf4_matmul<DT, FWD, DQ, OUT_F32, false>), dim3((unsigned)n), dim3(kGThreads),
+                               0, s, g);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (g.nsplit > 1) {
+        const int64_t n = g.M * g.ncol;
+        const int64_t blocks = (n / 4 + 255) / 256;
+        if (blocks > kMaxGemmGrid) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_splitk_sum<DT, OUT_F32>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           (const float*)g.part, g.nsplit, n, g.out);
+        return hipGetLastError();
     }
     return hipSuccess;
 }
 
 }  // namespace
 
+int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m)
+{
+    // With fewer output tiles than the chip has CUs, each workgroup walks the
+    // whole reduction one dependent k-step after another and the call is bound
+    // by that latency (0.083 ms for any m <= 256 on a 13824 x 5120 weight);
+    // then aim at about 1,024 (tile, split) workgroups, at most 16 splits of
+    // whole k-steps.  Measured on that weight: split at m <= 128 0.038-0.051 ms
+    // forward (dequantise + library GEMM 0.060-0.075), 0.063-0.070 backward
+    // (0.087-0.131); at 432 output tiles (m = 512 forward) a 3-way split was
+    // slower than none, so shapes with 256 tiles or more are not split.
+    const int64_t kred = forward ? cols : rows, ncol = forward ? rows : cols;
+    const int64_t tiles = ((m + kBM - 1) / kBM) * (ncol / kBN);
+    const int64_t ksteps = kred / kBK;
+    if (tiles >= 256 || ksteps < 2) return 1;
+    int64_t sp = (1024 + tiles - 1) / tiles;
+    if (sp > 16) sp = 16;
+    if (sp > ksteps) sp = ksteps;
+    const int64_t per = (ksteps + sp - 1) / sp;
+    return (int)((ksteps + per - 1) / per);
+}
+
 hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
                              const float* absmax, int64_t rows, int64_t cols, bool forward,
-                             const void* x, int64_t m, void* out, bool out_f32, hipStream_t s)
+                             const void* x, int64_t m, void* out, bool out_f32, float* part, int nsplit,
+                             hipStream_t s)
 {
     GemmArgs g;
     g.a = static_cast<const uint16_t*>(x);
@@ -403,6 +473,11 @@ hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabs
     g.ldo = g.ncol;
     g.ntn = g.ncol / kBN;
     g.tile0 = 0;
+    g.ntiles = ((m + kBM - 1) / kBM) * g.ntn;
+    const int ksteps = (int)(g.kred / kBK);
+    g.nsplit = (part && nsplit > 1) ? nsplit : 1;
+    g.split_steps = (ksteps + g.nsplit - 1) / g.nsplit;
+    g.part = part;
     const bool dq = qabsmax != nullptr;
 #define NF4_GEMM(T, F, D, O) return gemm_go<T, F, D, O>(g, s)
 #define NF4_GEMM_DT(T)                                                                             \

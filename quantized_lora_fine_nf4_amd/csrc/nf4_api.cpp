@@ -206,6 +206,44 @@ SelectLayout select_layout(int32_t nl)
     return L;
 }
 
+nf4_status check_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
+                        int32_t backward, const void* x, int64_t m, void* out, int32_t out_fp32)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    if (!w || !x || !out) return NF4_E_ARG;
+    if (rows <= 0 || cols <= 0 || m <= 0 || m >= (int64_t(1) << 31)) return NF4_E_ARG;
+    if (rows > kMaxN / cols || w->n != rows * cols) return NF4_E_ARG;
+    if (rows % 128 || cols % 128) return NF4_E_UNSUPPORTED;
+    if (backward != 0 && backward != 1) return NF4_E_ARG;
+    if (out_fp32 != 0 && out_fp32 != 1) return NF4_E_ARG;
+    const bool dq = fmt.dq_group != 0;
+    if (!w->codes || (dq ? (!w->qabsmax || !w->scale2) : !w->absmax)) return NF4_E_ARG;
+    if (!aligned(w->codes, 16) || !aligned(x, 16) || !aligned(out, 16)) return NF4_E_ALIGN;
+    if (dq ? !aligned(w->scale2, 4) : !aligned(w->absmax, 4)) return NF4_E_ALIGN;
+    return NF4_OK;
+}
+
+nf4_status run_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt, int32_t backward,
+                      const void* x, int64_t m, void* out, int32_t out_fp32, float* part, int nsplit,
+                      void* stream)
+{
+    const bool dq = fmt.dq_group != 0;
+    hipError_t e = nf4k::launch_nf4_matmul(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
+                                           dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax,
+                                           rows, cols, backward == 0, x, m, out, out_fp32 == 1,
+                                           part, nsplit, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
+// Bytes of fp32 partials for nsplit splits (0 without a split).
+size_t matmul_part_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m, int nsplit)
+{
+    if (nsplit <= 1) return 0;
+    const int64_t ncol = backward ? cols : rows;
+    return align256(size_t(nsplit) * size_t(m) * size_t(ncol) * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,27 +430,38 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
+
 nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                       int32_t backward, const void* x, int64_t m, void* out, int32_t out_fp32,
                       void* stream)
 {
-    nf4_status st = check_format(fmt);
+    nf4_status st = check_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32);
     if (st != NF4_OK) return st;
-    if (!w || !x || !out) return NF4_E_ARG;
-    if (rows <= 0 || cols <= 0 || m <= 0 || m >= (int64_t(1) << 31)) return NF4_E_ARG;
-    if (rows > kMaxN / cols || w->n != rows * cols) return NF4_E_ARG;
-    if (rows % 128 || cols % 128) return NF4_E_UNSUPPORTED;
-    if (backward != 0 && backward != 1) return NF4_E_ARG;
-    if (out_fp32 != 0 && out_fp32 != 1) return NF4_E_ARG;
-    const bool dq = fmt.dq_group != 0;
-    if (!w->codes || (dq ? (!w->qabsmax || !w->scale2) : !w->absmax)) return NF4_E_ARG;
-    if (!aligned(w->codes, 16) || !aligned(x, 16) || !aligned(out, 16)) return NF4_E_ALIGN;
-    if (dq ? !aligned(w->scale2, 4) : !aligned(w->absmax, 4)) return NF4_E_ALIGN;
-    hipError_t e = nf4k::launch_nf4_matmul(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
-                                           dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax,
-                                           rows, cols, backward == 0, x, m, out, out_fp32 == 1,
-                                           static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? NF4_OK : hip_fail(e);
+    return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, nullptr, 1, stream);
+}
+
+size_t nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m)
+{
+    if (rows <= 0 || cols <= 0 || m <= 0 || m >= (int64_t(1) << 31) || rows % 128 || cols % 128)
+        return 0;
+    if (rows > kMaxN / cols || (backward != 0 && backward != 1)) return 0;
+    return matmul_part_bytes(rows, cols, backward, m, nf4k::nf4_matmul_splits(rows, cols, backward == 0, m));
+}
+
+nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
+                         int32_t backward, const void* x, int64_t m, void* out, int32_t out_fp32,
+                         void* ws, size_t ws_bytes, void* stream)
+{
+    nf4_status st = check_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32);
+    if (st != NF4_OK) return st;
+    const int nsplit = nf4k::nf4_matmul_splits(rows, cols, backward == 0, m);
+    const size_t need = matmul_part_bytes(rows, cols, backward, m, nsplit);
+    if (need == 0)
+        return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, nullptr, 1, stream);
+    st = check_ws(ws, ws_bytes, need);
+    if (st != NF4_OK) return st;
+    return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, static_cast<float*>(ws), nsplit,
+                      stream);
 }
 
 size_t nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_variant v)

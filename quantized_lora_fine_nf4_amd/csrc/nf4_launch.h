@@ -40,10 +40,16 @@ hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups,
 // x[m x rows] * W; W [rows x cols] given by its codes and constants
 // (qabsmax + scale2 when qabsmax != nullptr, else absmax).  rows and cols
 // multiples of 128; x and the dequantised W in the 16-bit type dtype (0 bf16,
-// 1 fp16); out fp32 or that 16-bit type.
+// 1 fp16); out fp32 or that 16-bit type.  With part != nullptr and nsplit > 1
+// the reduction is split nsplit ways into fp32 partials at part
+// ([nsplit][m x (rows | cols)]), then added in split order into out.
 hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
                              const float* absmax, int64_t rows, int64_t cols, bool forward,
-                             const void* x, int64_t m, void* out, bool out_f32, hipStream_t s);
+                             const void* x, int64_t m, void* out, bool out_f32, float* part, int nsplit,
+                             hipStream_t s);
+// The split count the split-reduction matmul uses for a shape (1: none); a
+// function of the shape only.
+int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m);
 hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,
                          int kcap, uint8_t* selected, int32_t* k_out, int32_t* rank,
                          int32_t* perm, hipStream_t s);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(q.EXPORTS), set(names) ^ set(q.EXPORTS)
-    assert q.nf4_abi_version() == 2
+    assert q.nf4_abi_version() == 3
 
 
 def test_embedded_levels_and_thresholds_equal_the_oracles():
@@ -282,6 +282,37 @@ def test_matmul_arguments():
     assert call(out=FAKE + 8) == q.NF4_E_ALIGN
     assert call(s2=FAKE + 2) == q.NF4_E_ALIGN
     assert L.nf4_matmul(None, rows, cols, f, 0, FAKE, 10, FAKE, 1, None) == q.NF4_E_ARG
+
+
+def test_matmul_split_workspace_and_arguments():
+    """The split count depends on the shape only: the 14B FFN shape splits at
+    small m and not at m = 4096; the workspace is parts x m x ncol fp32 (256-B
+    rounded); a short or missing workspace is refused before anything is
+    enqueued, and the other checks are nf4_matmul's."""
+    L = q.lib()
+    f = q.fmt()
+    rows, cols = 13824, 5120
+    for backward in (0, 1):
+        ncol = cols if backward else rows
+        w16 = q.nf4_matmul_workspace_bytes(rows, cols, backward, 16)
+        assert w16 > 0 and w16 % 256 == 0 and w16 % (16 * ncol * 4) == 0
+        parts = w16 // (16 * ncol * 4)
+        assert 2 <= parts <= 16
+        assert q.nf4_matmul_workspace_bytes(rows, cols, backward, 4096) == 0
+    assert q.nf4_matmul_workspace_bytes(rows, cols, 0, 0) == 0
+    assert q.nf4_matmul_workspace_bytes(200, cols, 0, 16) == 0
+    assert L.nf4_matmul_workspace_bytes(rows, cols, 2, 16) == 0
+    lay = q.nf4_layer(rows * cols, None, FAKE, None, FAKE, FAKE, None)
+    need = q.nf4_matmul_workspace_bytes(rows, cols, 0, 16)
+
+    def call(ws=FAKE, wsb=need, m=16, backward=0, x=FAKE, fmt=f):
+        return L.nf4_matmul_ws(ctypes.byref(lay), rows, cols, fmt, backward, x, m, FAKE, 1, ws, wsb, None)
+    assert call(wsb=need - 1) == q.NF4_E_WORKSPACE
+    assert call(ws=None) == q.NF4_E_WORKSPACE
+    assert call(ws=FAKE + 16) == q.NF4_E_WORKSPACE
+    assert call(m=0) == q.NF4_E_ARG
+    assert call(x=FAKE + 8) == q.NF4_E_ALIGN
+    assert call(fmt=q.nf4_format(0, 32, 256)) == q.NF4_E_UNSUPPORTED
 
 
 def test_variant_helpers_and_arguments():

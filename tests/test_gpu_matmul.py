@@ -7,7 +7,8 @@ terms): |out - ref| <= 2 K 2^-24 (|x| |W|^T) elementwise.  The 16-bit output
 equals the round-to-nearest-even of the same kernel's fp32 output.  bf16 and
 fp16, ragged m (1, 77, 300), several tile counts, double quant on and off,
 forward and backward; the 14B stack's FFN shape (13824 x 5120) at m = 4096
-on sampled rows.
+on sampled rows.  The split-reduction path (nf4_matmul_ws) on shapes it
+splits, against the same bound, deterministic, and the FFN shape at m = 16.
 """
 import numpy as np
 import pytest
@@ -130,3 +131,61 @@ def test_matmul_fullsize_ffn_sampled(backward, dtype):
     idx = np.sort(np.r_[0, m - 1, rng.integers(0, m, 6)])
     worst = _check(out, xb, W, backward, rows_idx=idx)
     print(f"[{'bwd' if backward else 'fwd'}] worst error / bound {worst:.3f}", flush=True)
+
+
+def _run_ws(W, xb, backward, out_f32=True):
+    m = xb.shape[0]
+    ncol = W.cols if backward else W.rows
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    out = torch.full((m, ncol), float("nan"), dtype=torch.float32 if out_f32 else TORCH16[W.dtype],
+                     device="cuda")
+    need = q.nf4_matmul_workspace_bytes(W.rows, W.cols, backward, m)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+    if ws is not None:
+        ws.fill_(0xFF)   # stale NaN partials must not leak into the result
+    q.nf4_matmul_ws(W.layer, W.rows, W.cols, q.fmt(W.dtype, W.dq), x, out, ws, backward=backward)
+    torch.cuda.synchronize()
+    return out, need
+
+
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+@pytest.mark.parametrize("dtype", [BF16, FP16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("m", [1, 77, 300])
+def test_split_reduction_matches_oracle(m, dtype, backward):
+    """nf4_matmul_ws on shapes it splits (few output tiles): within the same
+    fp32 bound of the oracle's product, 16-bit output = RNE of its own fp32
+    result, and bitwise equal from run to run."""
+    rows, cols = 256, 384
+    print_case("nf4_matmul_ws", dtype, m, rows, cols, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 8100 + m, True, outliers=0.002, dtype=dtype)
+    xb = _x(m, rows if backward else cols, 13 * m + 1, dtype)
+    out, need = _run_ws(W, xb, backward)
+    assert need > 0
+    _check(out, xb, W, backward)
+    again, _ = _run_ws(W, xb, backward)
+    assert torch.equal(out, again)
+    o16, _ = _run_ws(W, xb, backward, out_f32=False)
+    assert torch.equal(o16, out.to(TORCH16[dtype]))
+
+
+def test_split_path_not_taken_equals_nf4_matmul():
+    """A shape whose output tiles fill the GPU needs no workspace, and then
+    nf4_matmul_ws is nf4_matmul bit for bit."""
+    W = DevWeight(4096, 128, 77, True)
+    xb = _x(2048, 128, 78)
+    out, need = _run_ws(W, xb, False)
+    assert need == 0
+    assert torch.equal(out, _run(W, xb, False))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_split_fullsize_ffn_small_m(backward):
+    rows, cols, m = 13824, 5120, 16
+    print_case("nf4_matmul_ws full size", rows, cols, m, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 101, True, outliers=0.0005)
+    xb = _x(m, rows if backward else cols, 102)
+    out, need = _run_ws(W, xb, backward)
+    assert need > 0
+    worst = _check(out, xb, W, backward)
+    print(f"[{'bwd' if backward else 'fwd'} m={m}] worst error / bound {worst:.3f}", flush=True)
