@@ -440,12 +440,14 @@ int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m)
     // then aim at about 1,024 (tile, split) workgroups, at most 16 splits of
     // whole k-steps.  Measured on that weight: split at m <= 128 0.038-0.051 ms
     // forward (dequantise + library GEMM 0.060-0.075), 0.063-0.070 backward
-    // (0.087-0.131); at 432 output tiles (m = 512 forward) a 3-way split was
-    // slower than none, so shapes with 256 tiles or more are not split.
+    // (0.087-0.131); at 432 output tiles and 80 k-steps (m = 512 forward) a
+    // 3-way split was slower than none, at 320 tiles and 216 k-steps (m = 1024
+    // backward) a 4-way split faster (0.327 against 0.477 ms): shapes are split
+    // below 256 tiles, or below 512 when the reduction has 128 k-steps or more.
     const int64_t kred = forward ? cols : rows, ncol = forward ? rows : cols;
     const int64_t tiles = ((m + kBM - 1) / kBM) * (ncol / kBN);
     const int64_t ksteps = kred / kBK;
-    if (tiles >= 256 || ksteps < 2) return 1;
+    if (ksteps < 2 || tiles >= 512 || (tiles >= 256 && ksteps < 128)) return 1;
     int64_t sp = (1024 + tiles - 1) / tiles;
     if (sp > 16) sp = 16;
     if (sp > ksteps) sp = ksteps;
