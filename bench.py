@@ -367,7 +367,8 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
                      "achieved": tf(t_fwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tf(t_fwd) / MFMA_BF16_PEAK_TFS, 4)},
     }
-    # few tokens: the split-reduction path against dequantise + library GEMM
+    # few tokens (nf4_matmul_ws: the few-token forward kernel at m <= 16, else
+    # the split reduction) against dequantise + library GEMM
     small = {}
     for ms in (16, 128):
         xs = torch.randn(ms, cols, dtype=torch.bfloat16, device="cuda", generator=gen)
@@ -383,7 +384,8 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
                                             backward=True))
         lf = timed(lambda: torch.matmul(xs, wt))
         lb = timed(lambda: torch.matmul(gs, w))
-        small[f"m{ms}"] = {"fused_split_fwd_ms": round(tf_, 4), "fused_split_bwd_ms": round(tb_, 4),
+        small[f"m{ms}"] = {"fused_ws_fwd_ms": round(tf_, 4), "fused_ws_bwd_ms": round(tb_, 4),
+                           "library_only_fwd_ms": round(lf, 4),
                            "dequant_then_library_fwd_ms": round(t_deq + lf, 4),
                            "dequant_then_library_bwd_ms": round(t_deq + lb, 4)}
         del xs, gs, ysf, ysb, wsf, wsb

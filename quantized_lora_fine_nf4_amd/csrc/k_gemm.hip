@@ -380,6 +380,118 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
             }
 }
 
+// ---- few tokens, forward: one wave per 16 W rows and one part of the reduction
+//
+// out[m x rows] = x[m x cols] W^T for m <= 16 on v_mfma_f32_16x16x32 (x rows
+// padded with zeros to 16).  The reduction is cut into 128-wide super-chunks;
+// in each, lane l takes W row n0 + l % 16 and x row l % 16 over the 32
+// consecutive k at 32 (l / 16), four MFMA steps of 8 k (any assignment of k
+// to steps gives the same dot product as long as x and W agree), so its
+// weight operand for a super-chunk is one 16-byte load of 32 codes from one
+// 64-weight block with one block constant.  A part is at most 8 super-chunks:
+// every wave issues all of its code and constant loads first, the workgroup
+// (four waves, one part, four row groups) stages the part's x slice in LDS,
+// and after one barrier the MFMAs run from registers and LDS.  Lane l ends
+// with output rows 4 (l / 16) + r of its W row; each part stores fp32
+// partials, added in part order by k_splitk_sum.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(const typename Frag8<DT>::T& a, const typename Frag8<DT>::T& b,
+                                        const f32x4& c)
+{
+    if constexpr (DT == 0) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+struct GemvArgs {
+    const uint16_t* x;      // [m x cols] 16-bit
+    const uint8_t* codes;   // W [rows x cols]
+    const int8_t* qabsmax;
+    const float* scale2;
+    const float* absmax;
+    int64_t rows, cols, m;
+    int64_t groups;         // rows / 16
+    int part_sc;            // 128-wide super-chunks per part (1..kGvMaxSc)
+    float* part;            // [parts][m x rows]
+};
+
+constexpr int kGvMaxSc = 8;                     // super-chunks per part
+constexpr int kGvRow = kGvMaxSc * 128 + 8;      // staged x row, 16-bit values (+16 B: rows on distinct banks)
+
+template <int DT, bool DQ>
+__global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
+{
+    __shared__ float s_lv[16];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[16 * kGvRow];
+    const int t = threadIdx.x, lane = t & 63;
+    const int part = blockIdx.y;
+    const int64_t grp = (int64_t)blockIdx.x * 4 + (t >> 6);
+    const bool live = grp < g.groups;           // wave-uniform; dead waves still meet the barrier
+    const int nsc = (int)(g.cols / 128);
+    const int s0 = part * g.part_sc;
+    const int ns = min(g.part_sc, nsc - s0);    // >= 1: the part count is ceil(nsc / part_sc)
+    const int64_t n = (live ? grp : 0) * 16 + (lane & 15);   // this lane's W row
+    const int kg = lane >> 4, xr = lane & 15;
+    // this lane's codes and block constants for the whole part
+    u32x4 cw[kGvMaxSc];
+    RawConst kc[kGvMaxSc];
+    const int64_t e0 = n * g.cols + (int64_t)s0 * 128 + 32 * kg;
+#pragma unroll
+    for (int sc = 0; sc < kGvMaxSc; ++sc) {
+        if (live && sc < ns) {
+            const int64_t e = e0 + 128 * sc;
+            cw[sc] = *(const GLOBAL u32x4*)(g.codes + (e >> 1));
+            const int64_t b = e >> 6;
+            if constexpr (DQ) kc[sc] = RawConst{((const GLOBAL int8_t*)g.qabsmax)[b], ((const GLOBAL float*)g.scale2)[b >> 8]};
+            else kc[sc] = RawConst{0, ((const GLOBAL float*)g.absmax)[b]};
+        }
+    }
+    // the part's x slice: rows < m, 16-byte units u = 128 row + column unit
+    if (t < 16) s_lv[t] = as_f(nf4fmt::kLevelBits[t]);
+    const int units = ns * 16;
+    u32x4 xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int u = t + 256 * i, r = u >> 7, c8 = u & 127;
+        if (r < g.m && c8 < units)
+            xv[i] = *(const GLOBAL u32x4*)((const GLOBAL uint16_t*)g.x + r * g.cols + (int64_t)s0 * 128 + 8 * c8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int u = t + 256 * i, r = u >> 7, c8 = u & 127;
+        if (r < g.m && c8 < units) *(u32x4*)(s_x + r * kGvRow + 8 * c8) = xv[i];
+    }
+    __syncthreads();
+    if (!live) return;
+    typedef typename Frag8<DT>::T F;
+    const bool xin = xr < g.m;
+    const uint16_t* xs = s_x + xr * kGvRow + 32 * kg;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sc = 0; sc < kGvMaxSc; ++sc) {
+        if (sc >= ns) break;
+        const float adq = block_const<DQ>(kc[sc]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 w;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t b = (cw[sc][j] >> (8 * h)) & 255u;
+                w[h] = pack16<DT>(s_lv[b & 15] * adq, s_lv[b >> 4] * adq);
+            }
+            const u32x4 a = xin ? *(const u32x4*)(xs + 128 * sc + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+            acc = mfma16<DT>(__builtin_bit_cast(F, a), __builtin_bit_cast(F, w), acc);
+        }
+    }
+    GLOBAL float* dst = (GLOBAL float*)g.part + (int64_t)part * g.m * g.rows;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * kg + r;
+        if (row < g.m) dst[(int64_t)row * g.rows + n] = acc[r];
+    }
+}
+
 // The fp32 partials of the splits added in split order (fixed, so the result
 // does not depend on timing), stored as fp32 or rounded to the 16-bit type.
 // Four outputs per thread; n is a multiple of 4 (ncol is a multiple of 128).
@@ -453,6 +565,70 @@ int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m)
     if (sp > ksteps) sp = ksteps;
     const int64_t per = (ksteps + sp - 1) / sp;
     return (int)((ksteps + per - 1) / per);
+}
+
+namespace {
+
+// Super-chunks per part: about 2,048 (row group, part) waves, at most
+// kGvMaxSc super-chunks each.
+int gemv_part_sc(int64_t rows, int64_t cols)
+{
+    const int64_t groups = rows / 16, nsc = cols / 128;
+    int64_t sc = nsc * groups / 2048;
+    return (int)(sc < 1 ? 1 : sc > kGvMaxSc ? kGvMaxSc : sc);
+}
+
+}  // namespace
+
+int nf4_gemv_parts(int64_t rows, int64_t cols, bool forward, int64_t m)
+{
+    if (!forward || m > 16) return 0;
+    const int64_t sc = gemv_part_sc(rows, cols), nsc = cols / 128;
+    return (int)((nsc + sc - 1) / sc);
+}
+
+namespace {
+
+template <int DT, bool DQ, bool OUT_F32>
+hipError_t gemv_go(const GemvArgs& g, int parts, void* out, hipStream_t s)
+{
+    const int64_t blocks = (g.groups + 3) / 4;
+    if (blocks > kMaxGemmGrid || parts > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_nf4_gemv16<DT, DQ>), dim3((unsigned)blocks, (unsigned)parts), dim3(256), 0, s, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = g.m * g.rows;
+    hipLaunchKernelGGL((k_splitk_sum<DT, OUT_F32>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                       (const float*)g.part, parts, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_nf4_gemv(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
+                           const float* absmax, int64_t rows, int64_t cols, const void* x, int64_t m,
+                           void* out, bool out_f32, float* part, int parts, hipStream_t s)
+{
+    GemvArgs g;
+    g.x = static_cast<const uint16_t*>(x);
+    g.codes = codes;
+    g.qabsmax = qabsmax;
+    g.scale2 = scale2;
+    g.absmax = absmax;
+    g.rows = rows;
+    g.cols = cols;
+    g.m = m;
+    g.groups = rows / 16;
+    g.part_sc = gemv_part_sc(rows, cols);
+    if ((cols / 128 + g.part_sc - 1) / g.part_sc != parts) return hipErrorInvalidValue;
+    g.part = part;
+    const bool dq = qabsmax != nullptr;
+    if (dtype == 0) {
+        if (dq) return out_f32 ? gemv_go<0, true, true>(g, parts, out, s) : gemv_go<0, true, false>(g, parts, out, s);
+        return out_f32 ? gemv_go<0, false, true>(g, parts, out, s) : gemv_go<0, false, false>(g, parts, out, s);
+    }
+    if (dq) return out_f32 ? gemv_go<1, true, true>(g, parts, out, s) : gemv_go<1, true, false>(g, parts, out, s);
+    return out_f32 ? gemv_go<1, false, true>(g, parts, out, s) : gemv_go<1, false, false>(g, parts, out, s);
 }
 
 hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,

@@ -445,6 +445,8 @@ size_t nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, 
     if (rows <= 0 || cols <= 0 || m <= 0 || m >= (int64_t(1) << 31) || rows % 128 || cols % 128)
         return 0;
     if (rows > kMaxN / cols || (backward != 0 && backward != 1)) return 0;
+    const int gv = nf4k::nf4_gemv_parts(rows, cols, backward == 0, m);
+    if (gv > 0) return align256(size_t(gv) * size_t(m) * size_t(rows) * sizeof(float));
     return matmul_part_bytes(rows, cols, backward, m, nf4k::nf4_matmul_splits(rows, cols, backward == 0, m));
 }
 
@@ -454,6 +456,17 @@ nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_for
 {
     nf4_status st = check_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32);
     if (st != NF4_OK) return st;
+    const int gv = nf4k::nf4_gemv_parts(rows, cols, backward == 0, m);
+    if (gv > 0) {
+        st = check_ws(ws, ws_bytes, nf4_matmul_workspace_bytes(rows, cols, backward, m));
+        if (st != NF4_OK) return st;
+        const bool dq = fmt.dq_group != 0;
+        hipError_t e = nf4k::launch_nf4_gemv(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
+                                             dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax, rows, cols,
+                                             x, m, out, out_fp32 == 1, static_cast<float*>(ws), gv,
+                                             static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? NF4_OK : hip_fail(e);
+    }
     const int nsplit = nf4k::nf4_matmul_splits(rows, cols, backward == 0, m);
     const size_t need = matmul_part_bytes(rows, cols, backward, m, nsplit);
     if (need == 0)

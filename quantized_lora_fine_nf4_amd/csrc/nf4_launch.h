@@ -50,6 +50,14 @@ hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabs
 // The split count the split-reduction matmul uses for a shape (1: none); a
 // function of the shape only.
 int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m);
+// Few-token forward (m <= 16): the part count of the wave-per-16-rows path
+// (0 when it does not apply); a function of the shape only.
+int nf4_gemv_parts(int64_t rows, int64_t cols, bool forward, int64_t m);
+// That path: fp32 partials at part ([parts][m x rows]), then added in part
+// order into out (fp32 or the 16-bit type dtype).
+hipError_t launch_nf4_gemv(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
+                           const float* absmax, int64_t rows, int64_t cols, const void* x, int64_t m,
+                           void* out, bool out_f32, float* part, int parts, hipStream_t s);
 hipError_t launch_select(const double* err, const int64_t* cost, int nl, int64_t budget,
                          int kcap, uint8_t* selected, int32_t* k_out, int32_t* rank,
                          int32_t* perm, hipStream_t s);

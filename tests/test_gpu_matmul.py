@@ -8,7 +8,8 @@ equals the round-to-nearest-even of the same kernel's fp32 output.  bf16 and
 fp16, ragged m (1, 77, 300), several tile counts, double quant on and off,
 forward and backward; the 14B stack's FFN shape (13824 x 5120) at m = 4096
 on sampled rows.  The split-reduction path (nf4_matmul_ws) on shapes it
-splits, against the same bound, deterministic, and the FFN shape at m = 16.
+splits, against the same bound, deterministic, and the FFN shape at m = 16;
+its few-token forward kernel (m <= 16: 1, 5, 16) the same way.
 """
 import numpy as np
 import pytest
@@ -165,6 +166,27 @@ def test_split_reduction_matches_oracle(m, dtype, backward):
     again, _ = _run_ws(W, xb, backward)
     assert torch.equal(out, again)
     o16, _ = _run_ws(W, xb, backward, out_f32=False)
+    assert torch.equal(o16, out.to(TORCH16[dtype]))
+
+
+@pytest.mark.parametrize("shape", [(256, 384), (128, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("dq", [False, True], ids=["nodq", "dq"])
+@pytest.mark.parametrize("dtype", [BF16, FP16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_few_token_forward_matches_oracle(m, dtype, dq, shape):
+    """nf4_matmul_ws forward with at most 16 tokens (one wave per 16 weight
+    rows, the reduction in parts): the same bound, 16-bit output = RNE of its
+    fp32 output, bitwise equal from run to run, and stale workspace unused."""
+    rows, cols = shape
+    print_case("nf4_matmul_ws few tokens", dtype, m, rows, cols, "dq" if dq else "nodq")
+    W = DevWeight(rows, cols, 8300 + m + rows, dq, outliers=0.002, dtype=dtype)
+    xb = _x(m, cols, 17 * m + rows, dtype)
+    out, need = _run_ws(W, xb, False)
+    assert need > 0 and need % 256 == 0
+    _check(out, xb, W, False)
+    again, _ = _run_ws(W, xb, False)
+    assert torch.equal(out, again)
+    o16, _ = _run_ws(W, xb, False, out_f32=False)
     assert torch.equal(o16, out.to(TORCH16[dtype]))
 
 
