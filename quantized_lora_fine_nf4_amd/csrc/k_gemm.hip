@@ -389,9 +389,10 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
 // to steps gives the same dot product as long as x and W agree), so its
 // weight operand for a super-chunk is one 16-byte load of 32 codes from one
 // 64-weight block with one block constant.  A part is at most 8 super-chunks:
-// every wave issues all of its code and constant loads first, the workgroup
-// (four waves, one part, four row groups) stages the part's x slice in LDS,
-// and after one barrier the MFMAs run from registers and LDS.  Lane l ends
+// every wave issues its share of the part's x slice and then all of its code
+// and constant loads, the workgroup (four waves, one part, four row groups)
+// stages the x slice in LDS, and after one barrier the MFMAs run from
+// registers and LDS, each super-chunk as soon as its codes have arrived.  Lane l ends
 // with output rows 4 (l / 16) + r of its W row; each part stores fp32
 // partials, added in part order by k_splitk_sum.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -426,36 +427,42 @@ __global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
     __shared__ __attribute__((aligned(16))) uint16_t s_x[16 * kGvRow];
     const int t = threadIdx.x, lane = t & 63;
     const int part = blockIdx.y;
-    const int64_t grp = (int64_t)blockIdx.x * 4 + (t >> 6);
-    const bool live = grp < g.groups;           // wave-uniform; dead waves still meet the barrier
+    const int64_t grp = (int64_t)blockIdx.x * 4 + (t >> 6);   // < groups: groups is a multiple of 4
     const int nsc = (int)(g.cols / 128);
     const int s0 = part * g.part_sc;
     const int ns = min(g.part_sc, nsc - s0);    // >= 1: the part count is ceil(nsc / part_sc)
-    const int64_t n = (live ? grp : 0) * 16 + (lane & 15);   // this lane's W row
+    const int64_t n = grp * 16 + (lane & 15);   // this lane's W row
     const int kg = lane >> 4, xr = lane & 15;
-    // this lane's codes and block constants for the whole part
+    // Every load below is unconditional and in bounds (a unit past the x slice
+    // or past row m - 1, or a super-chunk past the part, repeats the last valid
+    // one and is not used), so the compiler can wait for each super-chunk's
+    // loads alone and the MFMAs of the first super-chunks overlap the arrival
+    // of the later ones.  The x slice (cache-resident) goes first: waiting for
+    // it leaves the code loads in flight.
+    const int units = ns * 16;
+    const int64_t rmax = g.m - 1;
+    u32x4 xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int u = t + 256 * i;
+        const int64_t r = min((int64_t)(u >> 7), rmax);
+        const int c8 = min(u & 127, units - 1);
+        xv[i] = *(const GLOBAL u32x4*)((const GLOBAL uint16_t*)g.x + r * g.cols + (int64_t)s0 * 128 + 8 * c8);
+    }
     u32x4 cw[kGvMaxSc];
     RawConst kc[kGvMaxSc];
     const int64_t e0 = n * g.cols + (int64_t)s0 * 128 + 32 * kg;
 #pragma unroll
     for (int sc = 0; sc < kGvMaxSc; ++sc) {
-        if (live && sc < ns) {
-            const int64_t e = e0 + 128 * sc;
-            cw[sc] = *(const GLOBAL u32x4*)(g.codes + (e >> 1));
-            const int64_t b = e >> 6;
-            if constexpr (DQ) kc[sc] = RawConst{((const GLOBAL int8_t*)g.qabsmax)[b], ((const GLOBAL float*)g.scale2)[b >> 8]};
-            else kc[sc] = RawConst{0, ((const GLOBAL float*)g.absmax)[b]};
-        }
+        const int64_t e = e0 + 128 * min(sc, ns - 1);
+        cw[sc] = *(const GLOBAL u32x4*)(g.codes + (e >> 1));
+        const int64_t b = e >> 6;
+        if constexpr (DQ) kc[sc] = RawConst{((const GLOBAL int8_t*)g.qabsmax)[b], ((const GLOBAL float*)g.scale2)[b >> 8]};
+        else kc[sc] = RawConst{0, ((const GLOBAL float*)g.absmax)[b]};
     }
-    // the part's x slice: rows < m, 16-byte units u = 128 row + column unit
-    if (t < 16) s_lv[t] = as_f(nf4fmt::kLevelBits[t]);
-    const int units = ns * 16;
-    u32x4 xv[8];
+    if (t == 0) {   // immediates: an indexed table would be one more memory load to wait for
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int u = t + 256 * i, r = u >> 7, c8 = u & 127;
-        if (r < g.m && c8 < units)
-            xv[i] = *(const GLOBAL u32x4*)((const GLOBAL uint16_t*)g.x + r * g.cols + (int64_t)s0 * 128 + 8 * c8);
+        for (int i = 0; i < 16; ++i) s_lv[i] = as_f(nf4fmt::kLevelBits[i]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -463,7 +470,6 @@ __global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
         if (r < g.m && c8 < units) *(u32x4*)(s_x + r * kGvRow + 8 * c8) = xv[i];
     }
     __syncthreads();
-    if (!live) return;
     typedef typename Frag8<DT>::T F;
     const bool xin = xr < g.m;
     const uint16_t* xs = s_x + xr * kGvRow + 32 * kg;
@@ -619,6 +625,7 @@ hipError_t launch_nf4_gemv(int dtype, const uint8_t* codes, const int8_t* qabsma
     g.cols = cols;
     g.m = m;
     g.groups = rows / 16;
+    if (g.groups % 4 != 0 || m < 1 || m > 16) return hipErrorInvalidValue;   // whole workgroups of live waves
     g.part_sc = gemv_part_sc(rows, cols);
     if ((cols / 128 + g.part_sc - 1) / g.part_sc != parts) return hipErrorInvalidValue;
     g.part = part;
