@@ -149,6 +149,15 @@ __device__ __forceinline__ RawConst load_const(const GemmArgs& g, int64_t b)
     else return RawConst{0, ((const GLOBAL float*)g.absmax)[b]};
 }
 
+// Level c (0..15) by a select chain over immediates (no memory access).
+__device__ __forceinline__ float level_imm(int c)
+{
+    float v = as_f(nf4fmt::kLevelBits[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) v = c == i ? as_f(nf4fmt::kLevelBits[i]) : v;
+    return v;
+}
+
 // The dequantised constant (fl32 product with double quant).
 template <bool DQ>
 __device__ __forceinline__ float block_const(const RawConst& c)
@@ -276,16 +285,18 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
     __shared__ __attribute__((aligned(16))) uint16_t s_a[NF4_GEMM_STAGES][kBM * kLdp];
     __shared__ __attribute__((aligned(16))) uint16_t s_w[NF4_GEMM_STAGES][kBN * kLdp];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    // level tables from immediates: an indexed constant table would be a
+    // memory load, waited for before the first tile's loads are issued
 #if NF4_GEMM_LUT2
     __shared__ __attribute__((aligned(16))) float s_lv[2 * 256 * NF4_GEMM_LUT2];
     for (int i = t; i < 256 * NF4_GEMM_LUT2; i += kGThreads) {
         const int b = i & 255;
-        s_lv[2 * i] = as_f(nf4fmt::kLevelBits[b & 15]);
-        s_lv[2 * i + 1] = as_f(nf4fmt::kLevelBits[b >> 4]);
+        s_lv[2 * i] = level_imm(b & 15);
+        s_lv[2 * i + 1] = level_imm(b >> 4);
     }
 #else
     __shared__ float s_lv[16];
-    if (t < 16) s_lv[t] = as_f(nf4fmt::kLevelBits[t]);
+    if (t < 16) s_lv[t] = level_imm(t);
 #endif
 
     int64_t tile = g.tile0 + blockIdx.x;
