@@ -273,9 +273,10 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
  * m) bytes (NF4_E_WORKSPACE otherwise); when that is 0 the call is
  * nf4_matmul and ws may be NULL.  Error bound as for nf4_matmul:
  * (K/parts + parts) fp32 additions per output instead of K.  Forward with
- * m <= 16 takes a kernel of its own with the same contract: one wave per 16
- * weight rows and part of the reduction (parts of at most 1024 k), fp32
- * partials in ws added in part order by the same second kernel. */
+ * m <= 32 takes a kernel of its own with the same contract: one wave per 16
+ * weight rows and part of the reduction (parts of at most 1024 k, 512 k
+ * above 16 tokens), fp32 partials in ws added in part order by the same
+ * second kernel. */
 nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                          int32_t backward, const void* x, int64_t m, void* out,
                          int32_t out_fp32, void* ws, size_t ws_bytes, void* stream);

@@ -393,8 +393,8 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
 
 // ---- few tokens, forward: one wave per 16 W rows and one part of the reduction
 //
-// out[m x rows] = x[m x cols] W^T for m <= 16 on v_mfma_f32_16x16x32 (x rows
-// padded with zeros to 16).  The reduction is cut into 128-wide super-chunks;
+// out[m x rows] = x[m x cols] W^T for m <= 32 on v_mfma_f32_16x16x32 (x rows
+// padded with zeros to 16 or 32).  The reduction is cut into 128-wide super-chunks;
 // in each, lane l takes W row n0 + l % 16 and x row l % 16 over the 32
 // consecutive k at 32 (l / 16), four MFMA steps of 8 k (any assignment of k
 // to steps gives the same dot product as long as x and W agree), so its
@@ -428,14 +428,20 @@ struct GemvArgs {
     float* part;            // [parts][m x rows]
 };
 
-constexpr int kGvMaxSc = 8;                     // super-chunks per part
-constexpr int kGvRow = kGvMaxSc * 128 + 8;      // staged x row, 16-bit values (+16 B: rows on distinct banks)
+constexpr int kGvMaxSc = 8;   // super-chunks per part with one 16-row x block (MB = 1); 8 / MB with MB blocks
 
-template <int DT, bool DQ>
+// MB: 16-row blocks of x (m <= 16 MB); each dequantised weight fragment feeds
+// MB MFMAs.  The staged x slice is always 16 MB rows x (8 / MB) super-chunks
+// (33 KB of LDS, rows padded by 16 B so the 16 lanes of a row group read
+// distinct banks).
+template <int DT, bool DQ, int MB>
 __global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
 {
+    constexpr int kSc = kGvMaxSc / MB;          // super-chunks per part at most
+    constexpr int kRow = kSc * 128 + 8;         // staged x row, 16-bit values
+    constexpr int kRowUnits = kSc * 16;         // 16-byte units of a staged row
     __shared__ float s_lv[16];
-    __shared__ __attribute__((aligned(16))) uint16_t s_x[16 * kGvRow];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[16 * MB * kRow];
     const int t = threadIdx.x, lane = t & 63;
     const int part = blockIdx.y;
     const int64_t grp = (int64_t)blockIdx.x * 4 + (t >> 6);   // < groups: groups is a multiple of 4
@@ -456,15 +462,15 @@ __global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int u = t + 256 * i;
-        const int64_t r = min((int64_t)(u >> 7), rmax);
-        const int c8 = min(u & 127, units - 1);
+        const int64_t r = min((int64_t)(u / kRowUnits), rmax);
+        const int c8 = min(u % kRowUnits, units - 1);
         xv[i] = *(const GLOBAL u32x4*)((const GLOBAL uint16_t*)g.x + r * g.cols + (int64_t)s0 * 128 + 8 * c8);
     }
-    u32x4 cw[kGvMaxSc];
-    RawConst kc[kGvMaxSc];
+    u32x4 cw[kSc];
+    RawConst kc[kSc];
     const int64_t e0 = n * g.cols + (int64_t)s0 * 128 + 32 * kg;
 #pragma unroll
-    for (int sc = 0; sc < kGvMaxSc; ++sc) {
+    for (int sc = 0; sc < kSc; ++sc) {
         const int64_t e = e0 + 128 * min(sc, ns - 1);
         cw[sc] = *(const GLOBAL u32x4*)(g.codes + (e >> 1));
         const int64_t b = e >> 6;
@@ -477,16 +483,16 @@ __global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int u = t + 256 * i, r = u >> 7, c8 = u & 127;
-        if (r < g.m && c8 < units) *(u32x4*)(s_x + r * kGvRow + 8 * c8) = xv[i];
+        const int u = t + 256 * i, r = u / kRowUnits, c8 = u % kRowUnits;
+        if (r < g.m && c8 < units) *(u32x4*)(s_x + r * kRow + 8 * c8) = xv[i];
     }
     __syncthreads();
     typedef typename Frag8<DT>::T F;
-    const bool xin = xr < g.m;
-    const uint16_t* xs = s_x + xr * kGvRow + 32 * kg;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[MB];
 #pragma unroll
-    for (int sc = 0; sc < kGvMaxSc; ++sc) {
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sc = 0; sc < kSc; ++sc) {
         if (sc >= ns) break;
         const float adq = block_const<DQ>(kc[sc]);
 #pragma unroll
@@ -497,16 +503,24 @@ __global__ __launch_bounds__(256, 4) void k_nf4_gemv16(GemvArgs g)
                 const uint32_t b = (cw[sc][j] >> (8 * h)) & 255u;
                 w[h] = pack16<DT>(s_lv[b & 15] * adq, s_lv[b >> 4] * adq);
             }
-            const u32x4 a = xin ? *(const u32x4*)(xs + 128 * sc + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-            acc = mfma16<DT>(__builtin_bit_cast(F, a), __builtin_bit_cast(F, w), acc);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int xrow = 16 * mb + xr;
+                const u32x4 a = xrow < g.m ? *(const u32x4*)(s_x + xrow * kRow + 32 * kg + 128 * sc + 8 * j)
+                                           : u32x4{0u, 0u, 0u, 0u};
+                acc[mb] = mfma16<DT>(__builtin_bit_cast(F, a), __builtin_bit_cast(F, w), acc[mb]);
+            }
         }
     }
+    // lane l: output rows 16 mb + 4 (l / 16) + r of W row n
     GLOBAL float* dst = (GLOBAL float*)g.part + (int64_t)part * g.m * g.rows;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * kg + r;
-        if (row < g.m) dst[(int64_t)row * g.rows + n] = acc[r];
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mb + 4 * kg + r;
+            if (row < g.m) dst[(int64_t)row * g.rows + n] = acc[mb][r];
+        }
 }
 
 // The fp32 partials of the splits added in split order (fixed, so the result
@@ -587,20 +601,22 @@ int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m)
 namespace {
 
 // Super-chunks per part: about 2,048 (row group, part) waves, at most
-// kGvMaxSc super-chunks each.
-int gemv_part_sc(int64_t rows, int64_t cols)
+// kGvMaxSc / mb super-chunks each (mb: 16-row blocks of x).
+int gemv_part_sc(int64_t rows, int64_t cols, int mb)
 {
-    const int64_t groups = rows / 16, nsc = cols / 128;
+    const int64_t groups = rows / 16, nsc = cols / 128, cap = kGvMaxSc / mb;
     int64_t sc = nsc * groups / 2048;
-    return (int)(sc < 1 ? 1 : sc > kGvMaxSc ? kGvMaxSc : sc);
+    return (int)(sc < 1 ? 1 : sc > cap ? cap : sc);
 }
+
+int gemv_blocks(int64_t m) { return m <= 16 ? 1 : 2; }
 
 }  // namespace
 
 int nf4_gemv_parts(int64_t rows, int64_t cols, bool forward, int64_t m)
 {
-    if (!forward || m > 16) return 0;
-    const int64_t sc = gemv_part_sc(rows, cols), nsc = cols / 128;
+    if (!forward || m > 32) return 0;
+    const int64_t sc = gemv_part_sc(rows, cols, gemv_blocks(m)), nsc = cols / 128;
     return (int)((nsc + sc - 1) / sc);
 }
 
@@ -611,7 +627,9 @@ hipError_t gemv_go(const GemvArgs& g, int parts, void* out, hipStream_t s)
 {
     const int64_t blocks = (g.groups + 3) / 4;
     if (blocks > kMaxGemmGrid || parts > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_nf4_gemv16<DT, DQ>), dim3((unsigned)blocks, (unsigned)parts), dim3(256), 0, s, g);
+    const dim3 grid((unsigned)blocks, (unsigned)parts);
+    if (g.m <= 16) hipLaunchKernelGGL((k_nf4_gemv16<DT, DQ, 1>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_nf4_gemv16<DT, DQ, 2>), grid, dim3(256), 0, s, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = g.m * g.rows;
@@ -636,8 +654,8 @@ hipError_t launch_nf4_gemv(int dtype, const uint8_t* codes, const int8_t* qabsma
     g.cols = cols;
     g.m = m;
     g.groups = rows / 16;
-    if (g.groups % 4 != 0 || m < 1 || m > 16) return hipErrorInvalidValue;   // whole workgroups of live waves
-    g.part_sc = gemv_part_sc(rows, cols);
+    if (g.groups % 4 != 0 || m < 1 || m > 32) return hipErrorInvalidValue;   // whole workgroups of live waves
+    g.part_sc = gemv_part_sc(rows, cols, gemv_blocks(m));
     if ((cols / 128 + g.part_sc - 1) / g.part_sc != parts) return hipErrorInvalidValue;
     g.part = part;
     const bool dq = qabsmax != nullptr;

@@ -50,7 +50,7 @@ hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabs
 // The split count the split-reduction matmul uses for a shape (1: none); a
 // function of the shape only.
 int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m);
-// Few-token forward (m <= 16): the part count of the wave-per-16-rows path
+// Few-token forward (m <= 32): the part count of the wave-per-16-rows path
 // (0 when it does not apply); a function of the shape only.
 int nf4_gemv_parts(int64_t rows, int64_t cols, bool forward, int64_t m);
 // That path: fp32 partials at part ([parts][m x rows]), then added in part

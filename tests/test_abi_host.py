@@ -316,21 +316,22 @@ def test_matmul_split_workspace_and_arguments():
 
 
 def test_few_token_forward_workspace():
-    """Forward with m <= 16 takes the few-token kernel: parts of at most 8
-    super-chunks of 128 k, sized for about 2,048 (16-row group, part) waves,
-    so the workspace is ceil((cols/128) / sc) x m x rows fp32 with
-    sc = clamp((cols/128) (rows/16) / 2048, 1, 8); m = 17 and backward keep
-    the split reduction's count (at most 16 parts of whole k-steps)."""
+    """Forward with m <= 32 takes the few-token kernel: parts of at most 8
+    super-chunks of 128 k (4 above 16 tokens), sized for about 2,048 (16-row
+    group, part) waves, so the workspace is ceil((cols/128) / sc) x m x rows
+    fp32 with sc = clamp((cols/128) (rows/16) / 2048, 1, 8 or 4); m = 33 and
+    backward keep the split reduction's count (at most 16 parts of whole
+    k-steps)."""
     def expect(rows, cols, m):
         nsc, groups = cols // 128, rows // 16
-        sc = min(8, max(1, nsc * groups // 2048))
+        sc = min(8 if m <= 16 else 4, max(1, nsc * groups // 2048))
         parts = -(-nsc // sc)
         return -(-(parts * m * rows * 4) // 256) * 256
     for rows, cols in ((128, 128), (256, 384), (128, 1024), (8192, 1408), (13824, 5120),
                        (5120, 13824), (5120, 5120), (4096, 4096), (128, 65536)):
-        for m in (1, 5, 16):
+        for m in (1, 5, 16, 17, 32):
             assert q.nf4_matmul_workspace_bytes(rows, cols, False, m) == expect(rows, cols, m), (rows, cols, m)
-        for m, bwd in ((17, False), (16, True)):
+        for m, bwd in ((33, False), (16, True)):
             w = q.nf4_matmul_workspace_bytes(rows, cols, bwd, m)
             ncol = cols if bwd else rows
             parts = w // (m * ncol * 4)
@@ -339,6 +340,7 @@ def test_few_token_forward_workspace():
     # one part of 1..8 super-chunks covers a 128-wide reduction or the 14B FFN's 5120
     assert q.nf4_matmul_workspace_bytes(128, 128, False, 16) == 16 * 128 * 4
     assert q.nf4_matmul_workspace_bytes(13824, 5120, False, 16) == 5 * 16 * 13824 * 4
+    assert q.nf4_matmul_workspace_bytes(13824, 5120, False, 32) == 10 * 32 * 13824 * 4
 
 
 def test_variant_helpers_and_arguments():

@@ -8,8 +8,8 @@ equals the round-to-nearest-even of the same kernel's fp32 output.  bf16 and
 fp16, ragged m (1, 77, 300), several tile counts, double quant on and off,
 forward and backward; the 14B stack's FFN shape (13824 x 5120) at m = 4096
 on sampled rows.  The split-reduction path (nf4_matmul_ws) on shapes it
-splits, against the same bound, deterministic, and the FFN shape at m = 16;
-its few-token forward kernel (m <= 16: 1, 5, 16) the same way.
+splits, against the same bound, deterministic, and the FFN shape at m = 16
+and 32; its few-token forward kernel (m <= 32: 1, 5, 16, 17, 32) the same way.
 """
 import numpy as np
 import pytest
@@ -173,11 +173,12 @@ def test_split_reduction_matches_oracle(m, dtype, backward):
 @pytest.mark.parametrize("shape", [(256, 384), (128, 1024), (8192, 1408)], ids=lambda s: f"{s[0]}x{s[1]}")
 @pytest.mark.parametrize("dq", [False, True], ids=["nodq", "dq"])
 @pytest.mark.parametrize("dtype", [BF16, FP16], ids=["bf16", "fp16"])
-@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32])
 def test_few_token_forward_matches_oracle(m, dtype, dq, shape):
-    """nf4_matmul_ws forward with at most 16 tokens (one wave per 16 weight
-    rows, the reduction in parts): the same bound, 16-bit output = RNE of its
-    fp32 output, bitwise equal from run to run, and stale workspace unused."""
+    """nf4_matmul_ws forward with at most 32 tokens (one wave per 16 weight
+    rows and one or two 16-row blocks of x, the reduction in parts): the same
+    bound, 16-bit output = RNE of its fp32 output, bitwise equal from run to
+    run, and stale workspace unused."""
     rows, cols = shape
     print_case("nf4_matmul_ws few tokens", dtype, m, rows, cols, "dq" if dq else "nodq")
     W = DevWeight(rows, cols, 8300 + m + rows, dq, outliers=0.002, dtype=dtype)
@@ -202,9 +203,10 @@ def test_split_path_not_taken_equals_nf4_matmul():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("m", [16, 32])
 @pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
-def test_split_fullsize_ffn_small_m(backward):
-    rows, cols, m = 13824, 5120, 16
+def test_split_fullsize_ffn_small_m(backward, m):
+    rows, cols = 13824, 5120
     print_case("nf4_matmul_ws full size", rows, cols, m, "bwd" if backward else "fwd")
     W = DevWeight(rows, cols, 101, True, outliers=0.0005)
     xb = _x(m, rows if backward else cols, 102)
