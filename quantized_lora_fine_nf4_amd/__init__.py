@@ -240,8 +240,10 @@ def nf4_matmul_workspace_bytes(rows: int, cols: int, backward: bool, m: int) -> 
 
 def nf4_matmul_ws(layer, rows: int, cols: int, f: nf4_format, x, out, ws, backward: bool = False,
                   stream=None) -> None:
-    """nf4_matmul with a workspace (ws: device uint8 tensor or None) for the
-    split-reduction path of small m."""
+    """nf4_matmul with a workspace (ws: device uint8 tensor of at least
+    nf4_matmul_workspace_bytes(...) bytes, or None when that is 0) for small
+    m: the few-token forward kernel at m <= 32, else the split reduction
+    when the output tiles alone do not fill the GPU."""
     import torch
     m = int(x.shape[0]) if x.dim() > 1 else 1
     out_fp32 = 1 if out.dtype == torch.float32 else 0
