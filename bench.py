@@ -367,10 +367,10 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
                      "achieved": tf(t_fwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tf(t_fwd) / MFMA_BF16_PEAK_TFS, 4)},
     }
-    # few tokens (nf4_matmul_ws: the few-token forward kernel at m <= 16, else
+    # few tokens (nf4_matmul_ws: the few-token forward kernel at m <= 32, else
     # the split reduction) against dequantise + library GEMM
     small = {}
-    for ms in (16, 128):
+    for ms in (16, 32, 128):
         xs = torch.randn(ms, cols, dtype=torch.bfloat16, device="cuda", generator=gen)
         gs = torch.randn(ms, rows, dtype=torch.bfloat16, device="cuda", generator=gen)
         ysf = torch.empty(ms, rows, dtype=torch.bfloat16, device="cuda")
