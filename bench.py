@@ -384,7 +384,11 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
                                             backward=True))
         lf = timed(lambda: torch.matmul(xs, wt))
         lb = timed(lambda: torch.matmul(gs, w))
+        # algorithmic bytes of the forward call: codes, int8 constants, scale2, x, out
+        fbytes = rows * cols // 2 + rows * cols // 64 + rows * cols // 64 // 256 * 4 + 2 * ms * (cols + rows)
         small[f"m{ms}"] = {"fused_ws_fwd_ms": round(tf_, 4), "fused_ws_bwd_ms": round(tb_, 4),
+                           "fused_ws_fwd_GBps": round(fbytes / (tf_ * 1e-3) / 1e9, 1),
+                           "fused_ws_fwd_frac_of_hbm_peak": round(fbytes / (tf_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "library_only_fwd_ms": round(lf, 4),
                            "dequant_then_library_fwd_ms": round(t_deq + lf, 4),
                            "dequant_then_library_bwd_ms": round(t_deq + lb, 4)}
