@@ -156,19 +156,28 @@ void nf4o_to16_rne_array(const float* f, int64_t n, int dtype, uint16_t* out)
  * values.  Code order is ascending level order; code = #{i : t_i < s}.  Values
  * slightly beyond +-1 (from rounding of the normalisation) saturate to the end
  * codes by themselves. */
-int nf4o_encode(float s)
+/* The thresholds are computed by the caller and passed in (no static table),
+ * so the oracle keeps no state between calls and may run on several threads
+ * at once, one matrix per thread. */
+static int encode_with(const float t[15], float s)
 {
-    static float t[15];
-    static int ready = 0;
-    if (!ready) { nf4o_thresholds(t); ready = 1; }
     int c = 0;
     for (int i = 0; i < 15; ++i) if (t[i] < s) ++c;
     return c;
 }
 
+int nf4o_encode(float s)
+{
+    float t[15];
+    nf4o_thresholds(t);
+    return encode_with(t, s);
+}
+
 void nf4o_encode_array(const float* s, int64_t n, uint8_t* out)
 {
-    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)nf4o_encode(s[i]);
+    float t[15];
+    nf4o_thresholds(t);
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)encode_with(t, s[i]);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -192,6 +201,8 @@ void nf4o_quantize(const uint16_t* w, int64_t n, int dtype,
                    uint8_t* codes, float* absmax)
 {
     const int64_t nb = (n + NF4O_BLOCK - 1) / NF4O_BLOCK;
+    float t[15];
+    nf4o_thresholds(t);
     memset(codes, 0, (size_t)((n + 1) / 2));
     for (int64_t b = 0; b < nb; ++b) {
         const int64_t lo = b * NF4O_BLOCK;
@@ -215,7 +226,7 @@ void nf4o_quantize(const uint16_t* w, int64_t n, int dtype,
             } else {
                 float x = nf4o_from16(w[i], dtype) * scale;
                 float s = x * r;
-                c = nf4o_encode(s);
+                c = encode_with(t, s);
             }
             codes[i >> 1] |= (uint8_t)(c << ((i & 1) * 4));
         }
@@ -521,6 +532,8 @@ double nf4o_layer_error_ex(const uint16_t* w, int64_t n, int dtype, int block, i
 {
     const int64_t nb = (n + block - 1) / block;
     const int64_t ng = (nb + NF4O_DQ_GROUP - 1) / NF4O_DQ_GROUP;
+    float t[15];
+    nf4o_thresholds(t);
     /* blockwise absmax and codes, exactly as nf4o_quantize with another block */
     memset(codes, 0, (size_t)((n + 1) / 2));
     for (int64_t b = 0; b < nb; ++b) {
@@ -537,7 +550,7 @@ double nf4o_layer_error_ex(const uint16_t* w, int64_t n, int dtype, int block, i
             r = 1.0f / (a * scale);
         }
         for (int64_t i = lo; i < hi; ++i) {
-            const int c = (a == 0.0f) ? 7 : nf4o_encode((nf4o_from16(w[i], dtype) * scale) * r);
+            const int c = (a == 0.0f) ? 7 : encode_with(t, (nf4o_from16(w[i], dtype) * scale) * r);
             codes[i >> 1] |= (uint8_t)(c << ((i & 1) * 4));
         }
     }

@@ -33,13 +33,25 @@ namespace {
 
 enum { BLOCK = 64, GROUP = 256, TILE = BLOCK * GROUP };
 
-static float g_lv[16], g_thr[15];
+// The level and threshold values, decoded from their bit patterns once, when
+// the library is loaded (namespace-scope initialisation runs before any call),
+// and only read afterwards: concurrent calls share them without a race.
+struct Tables {
+    float lv[16];
+    float thr[15];
+};
 
-static void init_tables(void)
+static Tables make_tables(void)
 {
-    for (int i = 0; i < 16; ++i) memcpy(&g_lv[i], &nf4fmt::kLevelBits[i], 4);
-    for (int i = 0; i < 15; ++i) memcpy(&g_thr[i], &nf4fmt::kThresholdBits[i], 4);
+    Tables t;
+    for (int i = 0; i < 16; ++i) memcpy(&t.lv[i], &nf4fmt::kLevelBits[i], 4);
+    for (int i = 0; i < 15; ++i) memcpy(&t.thr[i], &nf4fmt::kThresholdBits[i], 4);
+    return t;
 }
+
+static const Tables g_tables = make_tables();
+static const float* const g_lv = g_tables.lv;
+static const float* const g_thr = g_tables.thr;
 
 // The tile pass, compiled twice: for the portable target (x86-64-v3, AVX2)
 // and for AVX-512 (x86-64-v4: measured 25% faster per thread on an EPYC
@@ -94,7 +106,6 @@ nf4_status nf4_cpu_layer_error(const nf4_layer* layers, int32_t nl, nf4_format f
     const int64_t ntiles = first[nl];
     double* part = (double*)malloc(sizeof(double) * (size_t)ntiles);
     if (!part) { free(first); return NF4_E_ARG; }
-    init_tables();
     const bool wide = use_avx512();
     if (threads > 0) omp_set_num_threads(threads);
 #pragma omp parallel for schedule(dynamic, 8)

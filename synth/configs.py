@@ -86,13 +86,16 @@ S7B = StackConfig(
                ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)),
     dist=STUDENT_T4, budgets_gib=(0.2, 0.5, 1.0))
 
+# The 14B stack names no budget: 0.2 GiB (the quality setting's extra memory in
+# the AQLoRA abstract) is the one its step dequantises against; 0.5 and 1.0
+# GiB are also ranked, as for the 7B stack.
 S14B = StackConfig(
     cid=5, name="14B-shaped: 40 blocks d=5120 ffn=13824, bf16 N(0,0.02), 0.05% x10 outliers, "
-                "double quant, 0.2 GiB, dequant of unpromoted x2",
+                "double quant, 0.2 GiB (also 0.5 and 1.0 ranked), dequant of unpromoted x2",
     blocks=40,
     per_block=(("q", 5120, 5120), ("k", 5120, 5120), ("v", 5120, 5120), ("o", 5120, 5120),
                ("gate", 13824, 5120), ("up", 13824, 5120), ("down", 5120, 13824)),
-    outlier_frac=0.0005, budgets_gib=(0.2,), dequant_repeats=2)
+    outlier_frac=0.0005, budgets_gib=(0.2, 0.5, 1.0), dequant_repeats=2)
 
 CONFIGS = [TOY, SINGLE, S1P4B, S7B, S14B]
 BY_NAME = {"toy": TOY, "single": SINGLE, "1.4b": S1P4B, "7b": S7B, "14b": S14B}

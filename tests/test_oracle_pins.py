@@ -421,13 +421,18 @@ def test_selection_monotone_in_budget_and_error():
 def test_predicted_k_when_the_largest_matrices_rank_first(golden_dir):
     figs = json.load(open(os.path.join(golden_dir, "pages_figures.json")))
     gib = figs["quality_setting_extra_memory_gib"]["value"]
-    for cfg, expect in ((configs.S7B, {0.2: 3, 0.5: 8, 1.0: 16}), (configs.S14B, {0.2: 2})):
+    for cfg, expect in ((configs.S7B, {0.2: 3, 0.5: 8, 1.0: 16}),
+                        (configs.S14B, {0.2: 2, 0.5: 5, 1.0: 10})):
         sizes = np.array(cfg.sizes)
         cost = np.array([oracle.promote_cost(int(n), True) for n in sizes])
         err = sizes.astype(np.float64)     # larger matrix -> larger error
         for g, k in expect.items():
             _, K = oracle.select_topk(err, cost, int(g * (1 << 30)))
             assert K == k
+            # closed form: K whole FFN matrices, each costing 2n - (n/2 + n/64 + 4 n/16384)
+            ffn = int(sizes.max())
+            c_ffn = 2 * ffn - (ffn // 2 + ffn // 64 + 4 * (ffn // 16384))
+            assert k == int(g * (1 << 30)) // c_ffn
     assert gib == 0.2
 
 
