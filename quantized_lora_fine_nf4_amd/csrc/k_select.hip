@@ -1,9 +1,9 @@
 // k_select.hip -- AQLoRA's budgeted top-K on the device.
 //
-// "The pass ranks layers by NF4 reconstruction error and keeps the top-K in
-// fp16 under a memory budget" (AQLoRA listing, arxivdaily.com, English
-// abstract); the budget is configurable ("AQLoRA: A Zero-Search Recipe...",
-// aitrending.vip, Technical Details).  Order: error descending, equal errors
+// AQLoRA orders the matrices by their NF4 reconstruction error and keeps the
+// leading ones in 16 bits while a memory budget allows (AQLoRA listing,
+// arxivdaily.com, English abstract); the budget is a setting ("AQLoRA: A
+// Zero-Search Recipe...", aitrending.vip, Technical Details).  Order: error descending, equal errors
 // by layer index ascending (a strict total order, so the ranking is unique).
 // K = the longest prefix of that order whose running promotion cost stays
 // within the budget, capped by k_cap.
@@ -13,8 +13,8 @@
 // microseconds and needs no sort); k_take runs in one workgroup, scans the
 // costs in rank order and writes selected[] and K.
 //
-// Variants (the speed setting "adapts only the top blocks": AQLoRA listing,
-// English abstract): the ranked units may be groups of consecutive layers
+// Variants (the speed setting adapts only the highest-ranked blocks: AQLoRA
+// listing, English abstract): the ranked units may be groups of consecutive layers
 // (transformer blocks, promoted whole), each layer's error may be divided by
 // a per-layer denominator (n: mean squared error; sum of x^2: relative
 // error), and the budget may be filled past a unit that does not fit
