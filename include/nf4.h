@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NF4_ABI_VERSION 3
+#define NF4_ABI_VERSION 4
 
 typedef enum {
     NF4_OK = 0,
@@ -154,6 +154,26 @@ nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
  * touched. */
 nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                            double* err, void* ws, size_t ws_bytes, void* stream);
+
+/* nf4_layer_error without a workspace argument, for callers that cannot
+ * allocate device memory (code that must not call hipMalloc: graph capture,
+ * tight serving loops, harnesses that forbid it).  Same arguments, checks and
+ * results as nf4_layer_error (the same kernels); its workspace is a fixed
+ * file-scope device array of nf4_noalloc_scratch_bytes() (32 MiB) that each
+ * GPU holds from the first call on it until the process ends.  That bounds
+ * the call to table plus partials within 32 MiB: 64 bytes per matrix (rounded
+ * up to 256) plus 32 bytes per 16,384-weight tile (rounded up to 256), about
+ * 1.0e6 tiles or 1.7e10 weights; a larger call returns NF4_E_WORKSPACE before
+ * anything is enqueued.  Nothing is allocated or freed: no hipMalloc,
+ * hipFree or allocating library routine.  The scratch needs no clearing (the
+ * table is copied in and every partial is written before it is read).  Every
+ * call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (different streams, or host threads, without ordering between them) race
+ * and give undefined results; calls ordered on one stream are safe. */
+nf4_status nf4_layer_error_noalloc(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                                   double* err, void* stream);
+/* Size in bytes of nf4_layer_error_noalloc's fixed per-device scratch. */
+size_t nf4_noalloc_scratch_bytes(void);
 
 /* nf4_layer_error plus sumsq[nl] (device fp64): the sum of x^2 over each
  * matrix, the denominator of the relative score err / sumsq.  The pages rank

@@ -72,6 +72,9 @@ EXPORTS = {
     "nf4_layer_error": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]),
+    "nf4_layer_error_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
+                                               ctypes.c_void_p, ctypes.c_void_p]),
+    "nf4_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "nf4_layer_error_norm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
@@ -191,6 +194,18 @@ def nf4_layer_error(layers, f: nf4_format, err, ws, stream=None) -> None:
     _check(lib().nf4_layer_error(arr, nl, f, _ptr(err), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "nf4_layer_error")
+
+
+def nf4_layer_error_noalloc(layers, f: nf4_format, err, stream=None) -> None:
+    """nf4_layer_error with the library's fixed per-device scratch instead of
+    a workspace (for callers that cannot allocate)."""
+    arr, nl = _layers_arg(layers)
+    _check(lib().nf4_layer_error_noalloc(arr, nl, f, _ptr(err), _stream(stream)),
+           "nf4_layer_error_noalloc")
+
+
+def nf4_noalloc_scratch_bytes() -> int:
+    return int(lib().nf4_noalloc_scratch_bytes())
 
 
 def aqlora_select_topk(err, cost, budget_bytes: int, k_cap: int, selected, k_out, ws,

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libnf4.so")
 CPU_LIB_PATH = os.path.join(PKG, "libnf4cpu.so")
 CPU_SOURCES = [os.path.join("cpu", "nf4_cpu.cpp")]
-SOURCES = ["k_codec.hip", "k_select.hip", "k_gemm.hip", "k_variants.hip", "nf4_api.cpp"]
+SOURCES = ["k_codec.hip", "k_select.hip", "k_gemm.hip", "k_variants.hip", "nf4_scratch.hip",
+           "nf4_api.cpp"]
 ARCH = os.environ.get("NF4_OFFLOAD_ARCH", "gfx950")
 
 

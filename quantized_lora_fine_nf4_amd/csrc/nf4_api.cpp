@@ -365,6 +365,30 @@ nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt, 
     return layer_error_impl(layers, nl, fmt, err, nullptr, ws, ws_bytes, stream);
 }
 
+nf4_status nf4_layer_error_noalloc(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                                   double* err, void* stream)
+{
+    // the same checks as nf4_layer_error, then the size check against the
+    // fixed scratch, all before anything is looked up or enqueued
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    const bool dq = fmt.dq_group != 0;
+    if (!err) return NF4_E_ARG;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl,
+                      NEED_W | NEED_CODES | (dq ? NEED_Q | NEED_S2 | OPT_ABSMAX : NEED_ABSMAX),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    if (!aligned(err, 8)) return NF4_E_ALIGN;
+    if (table_bytes(nl) + partial_bytes(ntiles) > nf4k::kScratchBytes) return NF4_E_WORKSPACE;
+    void* scratch = nullptr;
+    const hipError_t e = nf4k::scratch_pointer(&scratch);
+    if (e != hipSuccess) return hip_fail(e);
+    return layer_error_impl(layers, nl, fmt, err, nullptr, scratch, nf4k::kScratchBytes, stream);
+}
+
+size_t nf4_noalloc_scratch_bytes(void) { return nf4k::kScratchBytes; }
+
 nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
                                 double* sumsq, void* ws, size_t ws_bytes, void* stream)
 {

@@ -71,6 +71,12 @@ struct SelectScratch {
     int64_t* ucost;   // [nu]
     uint8_t* flag;    // [nu]
 };
+// The fixed device scratch of nf4_layer_error_noalloc (nf4_scratch.hip):
+// kScratchBytes per device.  scratch_pointer returns the current device's
+// copy, looked up once per device with hipGetSymbolAddress (thread-safe).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_pointer(void** out);
+
 hipError_t launch_select_ex(const double* err, const double* denom, const int64_t* cost,
                             const int32_t* group_end, int nu, int64_t budget, int kcap, int rule,
                             uint8_t* selected, int32_t* k_out, SelectScratch w, hipStream_t s);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(q.EXPORTS), set(names) ^ set(q.EXPORTS)
-    assert q.nf4_abi_version() == 3
+    assert q.nf4_abi_version() == 4
 
 
 def test_embedded_levels_and_thresholds_equal_the_oracles():
@@ -373,3 +373,29 @@ def test_variant_helpers_and_arguments():
     arr = (q.nf4_layer * 1)(_L(n=ns[0]))
     assert L.nf4_dequantize_variant(arr, 1, v, None, FAKE, need, None) == q.NF4_E_ARG
     assert L.nf4_dequantize_variant(arr, 1, q.variant(block=12), FAKE, FAKE, need, None) == q.NF4_E_UNSUPPORTED
+
+
+def test_noalloc_entry_checks_before_any_hip_call():
+    """nf4_layer_error_noalloc: the same argument checks as nf4_layer_error,
+    and a call whose table and partials exceed the fixed scratch is rejected
+    with NF4_E_WORKSPACE on the host (stand-in pointers, nothing enqueued)."""
+    L = q.lib()
+    f = q.fmt()
+    cap = q.nf4_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+
+    def call(layers, f=f, err=FAKE):
+        arr = (q.nf4_layer * max(1, len(layers)))(*layers)
+        return L.nf4_layer_error_noalloc(arr, len(layers), f, err, None)
+
+    assert call([_L()], err=None) == q.NF4_E_ARG
+    assert call([]) == q.NF4_E_ARG
+    assert call([_L(n=0)]) == q.NF4_E_ARG
+    assert call([_L(w=FAKE + 2)]) == q.NF4_E_ALIGN
+    assert call([_L()], err=FAKE + 4) == q.NF4_E_ALIGN
+    assert call([_L()], f=q.nf4_format(0, 32, 0)) == q.NF4_E_UNSUPPORTED
+    assert call([_L(qabsmax=None)]) == q.NF4_E_ARG
+    # tiles of 16,384 weights, 32 B of partials each, after the 256-byte table
+    tiles_max = (cap - 256) // 32
+    assert call([_L(n=(tiles_max + 1) * 16384)]) == q.NF4_E_WORKSPACE
+    assert call([_L(n=1 << 35)]) == q.NF4_E_WORKSPACE
