@@ -161,10 +161,10 @@ nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
  * results as nf4_layer_error (the same kernels); its workspace is a fixed
  * file-scope device array of nf4_noalloc_scratch_bytes() (32 MiB) that each
  * GPU holds from the first call on it until the process ends.  That bounds
- * the call to table plus partials within 32 MiB: 64 bytes per matrix (rounded
- * up to 256) plus 32 bytes per 16,384-weight tile (rounded up to 256), about
- * 1.0e6 tiles or 1.7e10 weights; a larger call returns NF4_E_WORKSPACE before
- * anything is enqueued.  Nothing is allocated or freed: no hipMalloc,
+ * the call to its workspace within 32 MiB: 64 bytes per matrix plus 8 bytes
+ * of tile record and 32 bytes of partials per 16,384-weight tile (each part
+ * rounded up to 256 bytes), about 8.4e5 tiles or 1.37e10 weights; a larger
+ * call returns NF4_E_WORKSPACE before anything is enqueued.  Nothing is allocated or freed: no hipMalloc,
  * hipFree or allocating library routine.  The scratch needs no clearing (the
  * table is copied in and every partial is written before it is read).  Every
  * call on one GPU shares that GPU's array, so calls that overlap on one GPU
@@ -309,8 +309,8 @@ nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_for
 size_t      nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m);
 
 /* Workspace for every codec call above over these matrices (the descriptor
- * table plus two arrays of 4 fp64 partials per 16384-weight tile); 0 on bad
- * input. */
+ * table, an 8-byte record per 16384-weight tile, and two arrays of 4 fp64
+ * partials per tile); 0 on bad input. */
 size_t      nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format fmt);
 /* Workspace for aqlora_select_topk and aqlora_select; 0 on bad input. */
 size_t      aqlora_workspace_bytes(int32_t nl);

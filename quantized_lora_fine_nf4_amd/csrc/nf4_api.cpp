@@ -81,6 +81,8 @@ size_t partial_bytes(int64_t ntiles)
 {
     return align256(size_t(ntiles) * nf4k::kPartsPerTile * sizeof(double));
 }
+// The fused pass's per-tile records (where each tile lies), after the table.
+size_t record_bytes(int64_t ntiles) { return align256(size_t(ntiles) * nf4k::kRecordBytes); }
 
 nf4_status check_ws(const void* ws, size_t ws_bytes, size_t need)
 {
@@ -169,17 +171,18 @@ nf4_status layer_error_impl(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                       &ntiles);
     if (st != NF4_OK) return st;
     if (!aligned(err, 8) || (sumsq && !aligned(sumsq, 8))) return NF4_E_ALIGN;
-    const size_t need = table_bytes(nl) + (sumsq ? 2 : 1) * partial_bytes(ntiles);
+    const size_t need = table_bytes(nl) + record_bytes(ntiles) + (sumsq ? 2 : 1) * partial_bytes(ntiles);
     if ((st = check_ws(ws, ws_bytes, need)) != NF4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     const LayerDesc* tab = static_cast<const LayerDesc*>(ws);
-    double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + table_bytes(nl));
+    char* rec = static_cast<char*>(ws) + table_bytes(nl);
+    double* partial = reinterpret_cast<double*>(rec + record_bytes(ntiles));
     double* partial_sq = sumsq ? reinterpret_cast<double*>(reinterpret_cast<char*>(partial) +
                                                            partial_bytes(ntiles))
                                : nullptr;
     hipError_t e = nf4k::launch_codec(tab, nl, ntiles, any_ragged(layers, nl), fmt.dtype, dq,
-                                      partial, partial_sq, s);
+                                      rec, partial, partial_sq, s);
     if (e != hipSuccess) return hip_fail(e);
     e = nf4k::launch_reduce(tab, nl, partial, err, s);
     if (e == hipSuccess && sumsq) e = nf4k::launch_reduce(tab, nl, partial_sq, sumsq, s);
@@ -297,7 +300,8 @@ size_t nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format f)
         ntiles += nf4k::tiles_of(n_per_layer[i]);
     }
     if (ntiles >= kMaxTiles) return 0;
-    return table_bytes(nl) + 2 * partial_bytes(ntiles);   // error and sum-of-squares partials
+    // tile records, then error and sum-of-squares partials
+    return table_bytes(nl) + record_bytes(ntiles) + 2 * partial_bytes(ntiles);
 }
 
 size_t aqlora_workspace_bytes(int32_t nl)
@@ -316,11 +320,12 @@ nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, voi
     st = check_layers(layers, nl, NEED_W | NEED_CODES | NEED_ABSMAX | (dq ? NEED_Q | NEED_S2 : 0u),
                       &ntiles);
     if (st != NF4_OK) return st;
-    if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + record_bytes(ntiles))) != NF4_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_codec(static_cast<const LayerDesc*>(ws), nl, ntiles,
-                                      any_ragged(layers, nl), fmt.dtype, dq, nullptr, nullptr, s);
+                                      any_ragged(layers, nl), fmt.dtype, dq,
+                                      static_cast<char*>(ws) + table_bytes(nl), nullptr, nullptr, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
@@ -380,7 +385,8 @@ nf4_status nf4_layer_error_noalloc(const nf4_layer* layers, int32_t nl, nf4_form
                       &ntiles);
     if (st != NF4_OK) return st;
     if (!aligned(err, 8)) return NF4_E_ALIGN;
-    if (table_bytes(nl) + partial_bytes(ntiles) > nf4k::kScratchBytes) return NF4_E_WORKSPACE;
+    if (table_bytes(nl) + record_bytes(ntiles) + partial_bytes(ntiles) > nf4k::kScratchBytes)
+        return NF4_E_WORKSPACE;
     void* scratch = nullptr;
     const hipError_t e = nf4k::scratch_pointer(&scratch);
     if (e != hipSuccess) return hip_fail(e);

@@ -12,9 +12,12 @@ namespace nf4k {
 // err_partial != nullptr, in-register dequantisation and the fp64 squared
 // error, written as kPartsPerTile partials per tile to err_partial; with
 // sq_partial != nullptr too, also the sum of x^2, laid out the same way.
+// rec_ws: device scratch for one 8-byte tile record per tile (kRecordBytes).
 // ragged: some layer's n is not a multiple of kTileElems (adds the tail launch).
+constexpr int kRecordBytes = 8;
 hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, int dtype,
-                        bool dq, double* err_partial, double* sq_partial, hipStream_t s);
+                        bool dq, void* rec_ws, double* err_partial, double* sq_partial,
+                        hipStream_t s);
 // Per-layer fixed-order sum of the per-tile partials into err[nl].
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
                          hipStream_t s);

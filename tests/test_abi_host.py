@@ -57,9 +57,10 @@ def test_workspace_sizes():
     f = q.fmt()
     ns = [16384 * 3 + 1, 100, 64]
     tiles = 4 + 1 + 1
-    # layer table (64 B per matrix) + 4 fp64 error partials and 4 fp64 sum-of-squares
-    # partials per tile of 16384 weights
-    assert q.nf4_workspace_bytes(ns, f) == 256 + 2 * (((tiles * 4 * 8 + 255) // 256) * 256)
+    # layer table (64 B per matrix) + an 8-byte record per tile of 16384 weights +
+    # 4 fp64 error partials and 4 fp64 sum-of-squares partials per tile
+    assert q.nf4_workspace_bytes(ns, f) == (256 + ((tiles * 8 + 255) // 256) * 256
+                                            + 2 * (((tiles * 4 * 8 + 255) // 256) * 256))
     assert q.nf4_workspace_bytes([], f) == 0
     assert q.nf4_workspace_bytes([0], f) == 0
     # rank, perm, staged group ends (int32), unit scores, unit costs (8 B), flags (1 B)
@@ -154,10 +155,13 @@ def test_workspace_checks(name):
     ns = [16384 * 5 + 3]
     tab_only = 256
     tiles = (ns[0] + 16383) // 16384
-    err_only = tab_only + ((tiles * 4 * 8 + 255) // 256) * 256   # table + error partials
-    assert q.nf4_workspace_bytes(ns, f) == tab_only + 2 * (err_only - tab_only)
-    # the dequantisation keeps a 32-byte record per tile where the fused pass keeps its partials
-    small = (tab_only - 1) if name in ("nf4_quantize", "nf4_double_quant") else (err_only - 1)
+    rec = ((tiles * 8 + 255) // 256) * 256                       # 8-byte tile records
+    part = ((tiles * 4 * 8 + 255) // 256) * 256                  # fp64 partials, 32 B per tile
+    assert q.nf4_workspace_bytes(ns, f) == tab_only + rec + 2 * part
+    # quantise: table + tile records; fused pass: + error partials; dequantisation: table +
+    # a 32-byte record per tile; double quant: table only
+    small = {"nf4_quantize": tab_only + rec, "nf4_double_quant": tab_only,
+             "nf4_layer_error": tab_only + rec + part, "nf4_dequantize": tab_only + part}[name] - 1
     assert _call(name, [_L(n=ns[0])], f, ws=None) == q.NF4_E_WORKSPACE
     assert _call(name, [_L(n=ns[0])], f, ws=FAKE + 64) == q.NF4_E_WORKSPACE
     assert _call(name, [_L(n=ns[0])], f, ws_bytes=small) == q.NF4_E_WORKSPACE
@@ -396,6 +400,6 @@ def test_noalloc_entry_checks_before_any_hip_call():
     assert call([_L()], f=q.nf4_format(0, 32, 0)) == q.NF4_E_UNSUPPORTED
     assert call([_L(qabsmax=None)]) == q.NF4_E_ARG
     # tiles of 16,384 weights, 32 B of partials each, after the 256-byte table
-    tiles_max = (cap - 256) // 32
+    tiles_max = (cap - 512) // 40
     assert call([_L(n=(tiles_max + 1) * 16384)]) == q.NF4_E_WORKSPACE
     assert call([_L(n=1 << 35)]) == q.NF4_E_WORKSPACE

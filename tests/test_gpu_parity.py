@@ -287,7 +287,10 @@ def test_workspace_writes_stay_inside_the_minimum_size(call):
     ls = layerset(ws_list, f)
     nl, ntiles = len(ls), sum((n + 16383) // 16384 for n in ls.ns)
     table = (nl * 64 + 255) // 256 * 256
-    need = table if call == "nf4_quantize" else table + (ntiles * 32 + 255) // 256 * 256
+    rec = (ntiles * 8 + 255) // 256 * 256      # the fused pass's 8-byte tile records
+    part = (ntiles * 32 + 255) // 256 * 256    # fp64 partials / dequantisation records
+    need = {"nf4_quantize": table + rec, "nf4_layer_error": table + rec + part,
+            "nf4_dequantize": table + part}[call]
     guard = 4096
     buf = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device="cuda")
     err = torch.empty(nl, dtype=torch.float64, device="cuda")
