@@ -115,16 +115,29 @@ __device__ void build_cells(EncCell* cells)
     }
 }
 
-// The same table (every replica) as a constant in device memory, computed at
+// The tables of the fused pass as one constant in device memory, computed at
 // compile time: the one-shot fused kernel copies it into LDS with 16-byte
 // loads instead of rebuilding it for every tile.
-struct CellTable {
-    EncCell c[kCells * kRepl];
+//   cells  the encode cells (every replica, as build_cells writes them);
+//   rcp    bf16 input: fl32(1 / (1 + m/128)) for the 7 mantissa bits m, so
+//          that fl32(1/a) = 2^-e rcp[m] for every normal a = 2^e (1 + m/128)
+//          (scaling by a power of two is exact);
+//   d127   fl32((1 + m/128) / 127), so that fl32(G/127) = 2^e d127[m] for the
+//          double-quant group maximum G = 2^e (1 + m/128), G >= 2^-100.
+struct CodecTables {
+    EncCell cells[kCells * kRepl];
+    uint32_t rcp[128];
+    uint32_t d127[128];
 };
 
-constexpr CellTable make_cell_table()
+constexpr CodecTables make_tables()
 {
-    CellTable t{};
+    CodecTables t{};
+    for (int m = 0; m < 128; ++m) {
+        const float mant = 1.0f + (float)m / 128.0f;
+        t.rcp[m] = __builtin_bit_cast(uint32_t, 1.0f / mant);
+        t.d127[m] = __builtin_bit_cast(uint32_t, mant / 127.0f);
+    }
     for (int idx = 0; idx < kCells * kRepl; ++idx) {
         const int k = idx / kRepl - 64;
         const float lo = (k > 0) ? (float)k : (k < 0 ? (float)(k - 1) : -1.0f);
@@ -136,13 +149,28 @@ constexpr CellTable make_cell_table()
             if (t64 < lo) ++base;
             else if (t64 <= hi) thr = t64;
         }
-        t.c[idx] = EncCell{thr, base};
+        t.cells[idx] = EncCell{thr, base};
     }
     return t;
 }
 
-__device__ const CellTable kCellTable = make_cell_table();
-static_assert(sizeof(CellTable) % 16 == 0, "copied in 16-byte units");
+// Padded to whole rounds of 256 lanes x 16 bytes, so the copy into LDS has no
+// guarded remainder (the padding is zeros and lands at the start of the
+// dequant table, which is cleared anyway).
+constexpr int kCopyRound = 256 * 16;
+constexpr int kCopyRounds = (int)((sizeof(CodecTables) + kCopyRound - 1) / kCopyRound);
+struct PaddedTables {
+    CodecTables t;
+    uint8_t pad[kCopyRounds * kCopyRound - sizeof(CodecTables)];
+};
+constexpr PaddedTables make_padded_tables()
+{
+    PaddedTables p{};
+    p.t = make_tables();
+    return p;
+}
+__device__ const PaddedTables kTables = make_padded_tables();
+static_assert(sizeof(PaddedTables) == kCopyRounds * kCopyRound, "whole copy rounds");
 
 // ---- 16-bit helpers ------------------------------------------------------
 
@@ -156,6 +184,33 @@ __device__ __forceinline__ uint32_t absmax_bits8(const u32x4 v)
     us2 r = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
                                       __builtin_elementwise_max(c, d));
     return r.x > r.y ? (uint32_t)r.x : (uint32_t)r.y;
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// The same through the packed fp16 maximum / minimum instructions, which take
+// three operands (two values each): the largest magnitude is max(max x, -min x).
+// For fp16 input that is the IEEE order of the values.  A bf16 bit pattern
+// read as fp16 orders the same way while it is not an fp16 NaN: the order of
+// IEEE values, infinities included, is the integer order of their 15
+// magnitude bits with the sign on top, as for bf16.  A bf16 |x| >= 2^121 reads
+// as an fp16 infinity or NaN, and a NaN would propagate, so a result at or
+// above the infinity pattern 0x7c00 is not trusted (the caller recomputes the
+// wave's maxima with absmax_bits8).
+// (A value, not a vector element: this compiler's __builtin_bit_cast of an
+// element access such as v.y was seen to read element 0 instead.)
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+
+__device__ __forceinline__ uint32_t absmax_bits8_f16ops(const u32x4 v)
+{
+    const h2 a = as_h2(v.x), b = as_h2(v.y), c = as_h2(v.z), d = as_h2(v.w);
+    const h2 mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                                __builtin_elementwise_maximum(c, d));
+    const h2 mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b),
+                                                __builtin_elementwise_minimum(c, d));
+    const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(mx, -mn));
+    const uint32_t lo = r & 0xffffu, hi = r >> 16;
+    return lo > hi ? lo : hi;
 }
 
 template <int DT>
@@ -361,7 +416,7 @@ __device__ __forceinline__ TileRef tile_ref(const LayerDesc* tab, int& l, int64_
 // tile parity so that a wave one tile ahead never overwrites a value another
 // wave still reads.
 struct CodecShared {
-    EncCell cells[kCells * kRepl];
+    CodecTables tab;            // copied from kTables (one-shot kernel) or built (tail kernel)
     float ytab[16 * kYStride];  // ytab[c * kYStride + b] = RNE16(level[c] * dequantised absmax of block b)
     uint32_t amax[256];         // block absmax bits (16-bit pattern)
     float r64[256];             // per block: 64 / absmax (of the 2^64-scaled absmax when tiny)
@@ -377,7 +432,12 @@ typedef uint16_t __attribute__((may_alias)) u16_alias;
 // dequant table's lower halves (zero; the tiles write only the upper halves).
 __device__ void init_shared(CodecShared& sh)
 {
-    build_cells(sh.cells);
+    build_cells(sh.tab.cells);
+    if (threadIdx.x < 128) {
+        const float mant = 1.0f + (float)threadIdx.x / 128.0f;
+        sh.tab.rcp[threadIdx.x] = __builtin_bit_cast(uint32_t, 1.0f / mant);
+        sh.tab.d127[threadIdx.x] = __builtin_bit_cast(uint32_t, mant / 127.0f);
+    }
     for (int i = threadIdx.x; i < 16 * kYStride; i += kCThreads) sh.ytab[i] = 0.0f;
 }
 
@@ -405,7 +465,7 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
                                                 const u32x4 (&v)[kCLoads], g_u8 cp, int valid)
 {
     const int lane = threadIdx.x & 63;
-    const EncCell* cells = sh.cells + (lane & (kRepl - 1));
+    const EncCell* cells = sh.tab.cells + (lane & (kRepl - 1));
     const uint32_t lb = lane_base<kCThreads>();
     // load j covers elements lb + 512 j ..: block (lb >> 6) + 8 j, code bytes
     // (lb >> 1) + 256 j; written as base + constant so that the constants
@@ -425,7 +485,7 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
             ek = sh.escale[bidx];
         }
         const uint32_t dw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        uint32_t pk = 0;
+        uint32_t cd[8];
         float eb = 0.0f, qb = 0.0f;
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {
@@ -453,9 +513,16 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
                         q = __builtin_fmaf(x[h], x[h], q);
                     }
                 }
-                pk |= code << (8 * k2 + 4 * h);
+                cd[2 * k2 + h] = code;
             }
         }
+        // element 2m in the low nibble of byte m: a shift-and-or per pair, then
+        // byte permutes (7 instructions per 8 codes)
+        const uint32_t b0 = cd[0] | (cd[1] << 4), b1 = cd[2] | (cd[3] << 4);
+        const uint32_t b2 = cd[4] | (cd[5] << 4), b3 = cd[6] | (cd[7] << 4);
+        const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);   // b0, b1, 0, 0
+        const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);   // b2, b3, 0, 0
+        uint32_t pk = __builtin_amdgcn_perm(hi, lo, 0x05040100u);   // b0, b1, b2, b3
         if constexpr (FULL) {
             store_stream(pk, (g_u32)(cp + (c0 + 256u * j)));
         } else {
@@ -536,43 +603,76 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
     // 2. block absmax (exact: a max of representable values), and the wave's
     //    largest for the double-quant group maximum
     const uint32_t b0 = lane_base<kCThreads>() >> 6;   // block of load j: b0 + 8 j
-    uint32_t wm = 0;
+    uint32_t m[kCLoads], wm = 0;
 #pragma unroll
     for (int j = 0; j < kCLoads; ++j) {
-        const uint32_t m = max8_u32(absmax_bits8(v[j]));
-        if ((lane & 7) == 0) sh.amax[b0 + 8u * j] = m;
-        wm = max(wm, m);
+        m[j] = max8_u32(absmax_bits8_f16ops(v[j]));
+        wm = max(wm, m[j]);
     }
-    if constexpr (DQ) {
+    if (DQ || DT == 0) wm = wave_max_u32(wm);
+    if (DT == 0 && wm >= 0x7c00u) {   // a bf16 |x| >= 2^121 somewhere in the wave's blocks
+        wm = 0;
+#pragma unroll
+        for (int j = 0; j < kCLoads; ++j) {
+            m[j] = max8_u32(absmax_bits8(v[j]));
+            wm = max(wm, m[j]);
+        }
         wm = wave_max_u32(wm);
+    }
+#pragma unroll
+    for (int j = 0; j < kCLoads; ++j)
+        if ((lane & 7) == 0) sh.amax[b0 + 8u * j] = m[j];
+    if constexpr (DQ) {
         if (lane == 0) sh.wmax[parity][wv] = wm;
         __syncthreads();   // the only workgroup barrier of a tile
     }
 
     // 3. constants of the wave's 64 blocks: lane L owns block b = 64 w + L = t
-    const float a = f16bits_to_f32<DT>(sh.amax[t]);
+    const uint32_t a16 = sh.amax[t];
+    const float a = f16bits_to_f32<DT>(a16);
     float adq = a;
-    int8_t q = 0;
+    float qk = 0.0f;
     float s2 = 0.0f;
     if constexpr (DQ) {
         uint32_t g = sh.wmax[parity][0];
 #pragma unroll
         for (int i = 1; i < kCWaves; ++i) g = max(g, sh.wmax[parity][i]);
+        g = __builtin_amdgcn_readfirstlane(g);
         const float G = f16bits_to_f32<DT>(g);
         if (G > 0.0f) {
-            s2 = G / 127.0f;
-            float qf = rintf(a / s2);
-            qf = fminf(fmaxf(qf, -127.0f), 127.0f);
-            q = (int8_t)qf;
-            adq = (float)q * s2;
+            if (DT == 0 && G >= 0x1p-100f) {
+                // scale2 = fl32(G/127) from the mantissa table; q = rint(fl32(a /
+                // scale2)): z = a * rcp(scale2) is within 2^-14 of fl32(a / scale2)
+                // (both within a few ulp of a / scale2 <= 127.5), so unless z lies
+                // within 2^-10 of a half-integer both round to the same integer;
+                // the lanes that do divide exactly.
+                s2 = __builtin_amdgcn_ldexpf(as_f(sh.tab.d127[g & 127u]), (int)(g >> 7) - 127);
+                const float z = a * __builtin_amdgcn_rcpf(s2);
+                qk = rintf(z);
+                const bool near = __builtin_fabsf(z - qk) > 0.5f - 0x1p-10f;
+                if (__builtin_amdgcn_ballot_w64(near) != 0 && near) qk = rintf(a / s2);
+            } else {
+                s2 = G / 127.0f;
+                qk = rintf(a / s2);
+            }
+            // a <= G, so fl32(a / scale2) < 127.5: the int8 clamp to +-127 never applies
+            adq = qk * s2;
         } else {
             adq = 0.0f;
         }
     }
-    // normalisation s = fl32(x * fl32(1/a)); carried as u = 64 s = x * (64/a)
+    // normalisation s = fl32(x * fl32(1/a)); carried as u = 64 s = x * (64/a).
+    // bf16 a in [2^-40, 2^40): fl32(1/a) = 2^-e rcp[m] exactly (a = 2^e (1 + m/128));
+    // the rest (rare) divides, with the prescale and error scaling below.
     float r64 = 0.0f, pre = 1.0f;
     int ek = 0;
-    if (a > 0.0f) {
+    const bool usual = DT == 0 ? (a16 - 0x2b80u < 0x2800u) : true;   // bf16 exponent field 87..166
+    if (usual) {
+        if constexpr (DT == 0)
+            r64 = __builtin_amdgcn_ldexpf(as_f(sh.tab.rcp[a16 & 127u]), 133 - (int)(a16 >> 7));
+        else
+            r64 = a > 0.0f ? (1.0f / a) * 64.0f : 0.0f;
+    } else if (a > 0.0f) {
         if (a < 0x1p-100f) {   // keeps 64/a finite; for normal a the codes are unchanged
             pre = 0x1p64f;
             r64 = (1.0f / (a * 0x1p64f)) * 64.0f;
@@ -592,12 +692,13 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
 #pragma unroll
         for (int c = 0; c < 16; c += 2) {
             float y0, y1;
-            const uint32_t p = round_pair<DT>(as_f(nf4fmt::kLevelBits[c]) * adq,
-                                              as_f(nf4fmt::kLevelBits[c + 1]) * adq, y0, y1);
+            // level 7 is 0 (its entries stay zero for bf16), levels 0 and 15 are -1 and +1
+            const float p1 = c + 1 == 7 ? 0.0f : as_f(nf4fmt::kLevelBits[c + 1]) * adq;
+            const uint32_t p = round_pair<DT>(as_f(nf4fmt::kLevelBits[c]) * adq, p1, y0, y1);
             if constexpr (DT == 0) {
                 u16_alias* yt = reinterpret_cast<u16_alias*>(sh.ytab);
                 yt[2 * (c * kYStride + t) + 1] = (uint16_t)p;
-                yt[2 * ((c + 1) * kYStride + t) + 1] = (uint16_t)(p >> 16);
+                if (c + 1 != 7) yt[2 * ((c + 1) * kYStride + t) + 1] = (uint16_t)(p >> 16);
             } else {
                 sh.ytab[c * kYStride + t] = y0;
                 sh.ytab[(c + 1) * kYStride + t] = y1;
@@ -609,7 +710,7 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
         const int64_t b = (tr.e0 >> 6) + t;
         if (t < nbv) {
             if (d.absmax) ((g_f32)d.absmax)[b] = a;
-            if constexpr (DQ) ((g_i8)d.qabsmax)[b] = q;
+            if constexpr (DQ) ((g_i8)d.qabsmax)[b] = (int8_t)(int)qk;
         }
         if constexpr (DQ) {
             if (t == 0) ((g_f32)d.scale2)[tr.local] = s2;
@@ -657,20 +758,37 @@ __global__ __launch_bounds__(kThreads) void k_codec_prep(const LayerDesc* __rest
 // LDS set-up of a one-shot workgroup: the encode cells copied from the
 // constant table (16 bytes per lane and load), and for bf16 the dequant
 // table's lower halves cleared (the tile writes only the upper halves).
-template <int DT>
-__device__ __forceinline__ void load_shared(CodecShared& sh)
+// The copy's loads are issued before the tile's weight loads, so that their
+// LDS writes wait only for them (memory operations complete in order).
+__device__ __forceinline__ void load_tables(u32x4 (&c)[kCopyRounds])
 {
-    constexpr int kChunks = (int)(sizeof(CellTable) / 16);
-    const GLOBAL u32x4* src = (const GLOBAL u32x4*)(const void*)&kCellTable;
-    u32x4* dst = reinterpret_cast<u32x4*>(sh.cells);
+    const GLOBAL u32x4* src = (const GLOBAL u32x4*)(const void*)&kTables;
 #pragma unroll
-    for (int i = threadIdx.x; i < kChunks; i += kCThreads) dst[i] = src[i];
+    for (int r = 0; r < kCopyRounds; ++r) c[r] = src[threadIdx.x + r * kCThreads];
+}
+
+// The tables into LDS, and for bf16 the dequant table's lower halves cleared
+// (the tile writes only the upper halves).  The copy's last round writes the
+// constant's zero padding over the start of the dequant table; the clearing
+// rounds start where it ends and run on over the constants that follow (the
+// per-block constants are written after the barrier that follows this).
+template <int DT>
+__device__ __forceinline__ void store_tables(CodecShared& sh, const u32x4 (&c)[kCopyRounds])
+{
+    static_assert(sizeof(CodecShared) >= kCopyRounds * kCopyRound + sizeof(float) * 16 * kYStride,
+                  "the copy and the clearing stay inside the workgroup's LDS");
+    const uint32_t t = threadIdx.x;
+    u32x4* dst = reinterpret_cast<u32x4*>(&sh.tab);
+#pragma unroll
+    for (int r = 0; r < kCopyRounds; ++r) dst[t + r * kCThreads] = c[r];
     if constexpr (DT == 0) {
-        static_assert((16 * kYStride * 4) % 16 == 0, "dequant table cleared in 16-byte units");
-        u32x4* y = reinterpret_cast<u32x4*>(sh.ytab);
+        constexpr int kCleared = kCopyRounds * kCopyRound - (int)sizeof(CodecTables);
+        constexpr int kZr = (int)((sizeof(float) * 16 * kYStride - kCleared + kCopyRound - 1) / kCopyRound);
+        static_assert(kCleared % 16 == 0, "16-byte units");
+        u32x4* y = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sh.ytab) + kCleared);
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = threadIdx.x; i < 16 * kYStride / 4; i += kCThreads) y[i] = z;
+        for (int r = 0; r < kZr; ++r) y[t + r * kCThreads] = z;
     }
 }
 
@@ -697,9 +815,10 @@ __global__ __launch_bounds__(kCThreads, ERR ? kCodecWavesPerEu : kQuantWavesPerE
     tr.local = r.local;
     tr.e0 = e0;
     tr.valid = kTileElems;
-    u32x4 v[kCLoads];
+    u32x4 c[kCopyRounds], v[kCLoads];
+    load_tables(c);
     load_tile<true>(v, tr);
-    load_shared<DT>(sh);
+    store_tables<DT>(sh, c);
     __syncthreads();
     codec_compute<DT, DQ, ERR, NORM, true>(sh, v, tr, tile, 0, partial, partial_sq);
 }
