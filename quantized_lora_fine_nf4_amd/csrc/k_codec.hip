@@ -21,6 +21,7 @@
 //   error       -- AQLoRA's per-layer NF4 reconstruction error (AQLoRA
 //                  listing, English abstract)
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "nf4_format.h"
@@ -37,9 +38,14 @@ constexpr int kCWaves = kWaves;
 constexpr int kCLoads = kLoads;
 static_assert(kPartsPerTile == kCWaves, "one fp64 error partial per wave and tile");
 constexpr int kCells = 129;                              // encode cells, trunc(64 s) in [-64, 64]
-constexpr int kRepl = 16;              // lane-indexed copies of the cell table: conflict-free 64-bit reads
+// Lane-indexed copies of the cell table (fewer bank conflicts on its 64-bit
+// reads).  Eight copies keep the fused kernel's LDS at 28.8 KB, 5 workgroups
+// per CU; measured on the 14B stack in one process: 16 copies (4 per CU)
+// 5.84 ms, 8 copies 5.53, 4 copies (6 per CU, registers spilled) 5.63,
+// 2 copies (7 per CU, spilled) 5.75.
+constexpr int kRepl = 8;
 constexpr int kYStride = 256 + 17;     // per-block dequant table, code-major, padded against bank conflicts
-constexpr int kCodecWavesPerEu = 4;    // schedule the fused pass for 128 VGPRs (4 workgroups per CU)
+constexpr int kCodecWavesPerEu = 4;    // register cap of the fused pass (5 fit: 91 VGPRs; LDS allows 5)
 constexpr int kQuantWavesPerEu = 3;    // the pass without the error (nf4_quantize): at 4 it spilled
 constexpr int kXcds = 8;             // accelerator dies (XCDs), each with its own L2 and translation caches
 
@@ -242,15 +248,11 @@ __device__ __forceinline__ float opaque(float x)
 }
 
 // Element offset of this lane's first weight within a tile (wave w of W,
-// lane L: (16384 / W) w + 8 L); load j adds 512 j.  Recomputed per tile behind an opaque
-// barrier: hoisted out of the tile loop, the 8 derived 64-bit addresses per
-// buffer would stay live across tiles and spill.
+// lane L: (16384 / W) w + 8 L); load j adds 512 j.
 template <int THREADS = kThreads>
 __device__ __forceinline__ uint32_t lane_base()
 {
-    uint32_t b = (threadIdx.x >> 6) * (uint32_t)(kTileElems / (THREADS / 64)) + (threadIdx.x & 63u) * 8u;
-    __asm__ volatile("" : "+v"(b));
-    return b;
+    return (threadIdx.x >> 6) * (uint32_t)(kTileElems / (THREADS / 64)) + (threadIdx.x & 63u) * 8u;
 }
 
 // Round two fp32 values to the 16-bit type (nearest, ties to even) and return
@@ -420,8 +422,6 @@ struct CodecShared {
     float ytab[16 * kYStride];  // ytab[c * kYStride + b] = RNE16(level[c] * dequantised absmax of block b)
     uint32_t amax[256];         // block absmax bits (16-bit pattern)
     float r64[256];             // per block: 64 / absmax (of the 2^64-scaled absmax when tiny)
-    float pre[256];             // per block: 2^64 when absmax < 2^-100, else 1
-    int escale[256];            // per block: k with absmax * 2^k in [1, 2) for extreme absmax, else 0
     uint32_t wmax[2][kCWaves];  // per tile parity, per wave: largest absmax bits of the wave's blocks
 };
 
@@ -481,8 +481,11 @@ __device__ __forceinline__ LaneSums encode_lane(const CodecShared& sh,
         float scale = 1.0f;
         int ek = 0;
         if constexpr (SPEC) {
-            scale = sh.pre[bidx];
-            ek = sh.escale[bidx];
+            // the rare path recomputes the block's prescale and error scaling
+            // from its absmax (the same rule as codec_compute)
+            const float a = f16bits_to_f32<DT>(sh.amax[bidx]);
+            scale = (a > 0.0f && a < 0x1p-100f) ? 0x1p64f : 1.0f;
+            ek = (ERR && a > 0.0f && (a < 0x1p-40f || a >= 0x1p40f)) ? 1 - __builtin_amdgcn_frexp_expf(a) : 0;
         }
         const uint32_t dw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t cd[8];
@@ -566,8 +569,11 @@ __device__ __forceinline__ void load_tile(u32x4 (&v)[kCLoads], const TileRef& tr
     const int valid = tr.valid;
     const uint32_t lb = lane_base<kCThreads>();
     if constexpr (FULL) {
+        // a uniform base plus a 32-bit lane offset plus an immediate: no 64-bit
+        // address arithmetic per load
+        const GLOBAL uint8_t* wb = (const GLOBAL uint8_t*)w;
 #pragma unroll
-        for (int j = 0; j < kCLoads; ++j) v[j] = load_stream((g_cu4)(w + (lb + j * 512u)));
+        for (int j = 0; j < kCLoads; ++j) v[j] = load_stream((g_cu4)(wb + (2u * lb + 1024u * j)));
     } else {
 #pragma unroll
         for (int j = 0; j < kCLoads; ++j) {
@@ -682,8 +688,6 @@ __device__ __forceinline__ void codec_compute(CodecShared& sh, const u32x4 (&v)[
         if (ERR && (a < 0x1p-40f || a >= 0x1p40f)) ek = 1 - __builtin_amdgcn_frexp_expf(a);
     }
     sh.r64[t] = r64;
-    sh.pre[t] = pre;
-    sh.escale[t] = ek;
     if constexpr (ERR) {
         // the block's 16 dequantised values, rounded to the 16-bit type, back in
         // fp32.  A bf16 value is the upper half of its fp32 pattern, so for bf16
@@ -770,25 +774,27 @@ __device__ __forceinline__ void load_tables(u32x4 (&c)[kCopyRounds])
 // The tables into LDS, and for bf16 the dequant table's lower halves cleared
 // (the tile writes only the upper halves).  The copy's last round writes the
 // constant's zero padding over the start of the dequant table; the clearing
-// rounds start where it ends and run on over the constants that follow (the
-// per-block constants are written after the barrier that follows this).
+// covers the rest of it.
 template <int DT>
 __device__ __forceinline__ void store_tables(CodecShared& sh, const u32x4 (&c)[kCopyRounds])
 {
-    static_assert(sizeof(CodecShared) >= kCopyRounds * kCopyRound + sizeof(float) * 16 * kYStride,
-                  "the copy and the clearing stay inside the workgroup's LDS");
+    constexpr int kCleared = kCopyRounds * kCopyRound - (int)sizeof(CodecTables);
+    static_assert(offsetof(CodecShared, ytab) == sizeof(CodecTables), "the dequant table follows the tables");
+    static_assert(kCleared % 16 == 0 && kCleared <= (int)sizeof(float) * 16 * kYStride,
+                  "the copy's padding lands inside the dequant table");
     const uint32_t t = threadIdx.x;
     u32x4* dst = reinterpret_cast<u32x4*>(&sh.tab);
 #pragma unroll
     for (int r = 0; r < kCopyRounds; ++r) dst[t + r * kCThreads] = c[r];
     if constexpr (DT == 0) {
-        constexpr int kCleared = kCopyRounds * kCopyRound - (int)sizeof(CodecTables);
-        constexpr int kZr = (int)((sizeof(float) * 16 * kYStride - kCleared + kCopyRound - 1) / kCopyRound);
-        static_assert(kCleared % 16 == 0, "16-byte units");
+        constexpr int kChunks = ((int)sizeof(float) * 16 * kYStride - kCleared) / 16;
+        constexpr int kZr = kChunks / kCThreads;
+        static_assert(((int)sizeof(float) * 16 * kYStride - kCleared) % 16 == 0, "16-byte units");
         u32x4* y = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(sh.ytab) + kCleared);
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int r = 0; r < kZr; ++r) y[t + r * kCThreads] = z;
+        if (t < (uint32_t)(kChunks - kZr * kCThreads)) y[t + kZr * kCThreads] = z;
     }
 }
 
