@@ -214,6 +214,36 @@ def hbm_probe(torch):
     return res
 
 
+def selections(q, torch, err, cost, cfg, stream, reps=20):
+    """aqlora_select_topk at every budget of the configuration, on the GPU's
+    scores of the last step: K, the relative score gap at the cut, and the
+    call's time (launches included)."""
+    import numpy as np
+    nl = int(err.numel())
+    sws = torch.empty(q.aqlora_workspace_bytes(nl), dtype=torch.uint8, device="cuda")
+    sel = torch.empty(nl, dtype=torch.uint8, device="cuda")
+    k = torch.empty(1, dtype=torch.int32, device="cuda")
+    errs = err.cpu().numpy()
+    order = np.lexsort((np.arange(nl), -errs))
+    res = {}
+    for g, b in zip(cfg.budgets_gib, cfg.budgets_bytes()):
+        q.aqlora_select_topk(err, cost, b, cfg.kcap, sel, k, sws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            q.aqlora_select_topk(err, cost, b, cfg.kcap, sel, k, sws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        K = int(k.item())
+        gap = None
+        if 0 < K < nl:
+            a, c = errs[order[K - 1]], errs[order[K]]
+            gap = float((a - c) / a)
+        res[f"{g} GiB"] = {"budget_bytes": b, "K": K, "relative_gap_at_cut": gap,
+                           "select_us": round(e0.elapsed_time(e1) / reps * 1e3, 1)}
+    return res
+
+
 def variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes, reps=10):
     """Selection variants on the same stack, after the timed steps: the fused
     pass that also returns the sum of squares (relative scores), and the
@@ -593,6 +623,8 @@ def main():
         "source_hash": source_hash(),
         "codec_source_hash": codec_source_hash(),
     }
+    if cfg.budgets_gib:
+        out["selections"] = selections(q, torch, err, cost, cfg, stream)
     if not args.no_variants:
         out["variants"] = variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes)
         if cfg.dtype == q.NF4_BF16 and cfg.dequant_repeats > 0 and all(
