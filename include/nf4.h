@@ -23,8 +23,9 @@
  *     fp32 ("absmax");
  *   - code of x = number of the 15 nearest-level thresholds strictly below
  *     s = fl32(x * fl32(1/absmax)); ascending level order, code 7 = 0.0;
- *     an all-zero block encodes to 7; blocks with absmax below 2^-126 are
- *     scaled by 2^64 first (exact);
+ *     an all-zero block encodes to 7 (for a subnormal absmax the oracle
+ *     scales x and absmax by 2^64 first, the kernels do so below 2^-100: an
+ *     exact power-of-two scaling that changes no code);
  *   - codes packed two per byte, element 2j in the low nibble of byte j, an
  *     odd final element leaves the high nibble 0;
  *   - double quantisation (dq_group = 256): per matrix, groups of 256
@@ -35,8 +36,15 @@
  *   - dequantised value = round-to-nearest-even to the input's 16-bit type of
  *     fl32(level[code] * constant);
  *   - reconstruction error of a matrix = sum over its elements of
- *     (x - dequantised x)^2, accumulated in fp32 within a block of 64 and in
- *     fp64 across blocks, in a fixed order (bitwise reproducible);
+ *     (x - dequantised x)^2.  The kernels accumulate it in fp32 over each
+ *     lane's 64 weights (8 consecutive weights from each of 8 blocks of one
+ *     wave's 64), then in fp64 across the lanes of a wave, the waves of a
+ *     16,384-weight tile and the tiles of the matrix, in a fixed order
+ *     (bitwise reproducible); in a wave where a block's absmax is below
+ *     2^-40 or at least 2^40 each difference is scaled by an exact power of
+ *     two before squaring and the lane's fp32 sum per block is unscaled in
+ *     fp64, so the squares neither underflow nor overflow.  Within 1e-5
+ *     relative of the oracle's exact fp64 sum (observed <= 2e-8);
  *   - promotion cost = 2n - NF4 bytes; ranking by error descending, equal
  *     errors by index ascending; K = the longest prefix of that order whose
  *     running cost stays within the budget (and within the count cap).
@@ -44,9 +52,10 @@
  * Conventions for every call:
  *   - Buffers named "device" are device pointers the caller allocated and
  *     owns; the library never allocates or frees device memory and keeps no
- *     pointer after it returns.  `stream` is a hipStream_t (NULL = the null
- *     stream); calls only enqueue work on it and return -- the caller
- *     synchronises.  Every device buffer must stay alive until that work is
+ *     pointer after it returns (nf4_layer_error_noalloc uses a fixed device
+ *     array of the library instead of a workspace).  `stream` is a
+ *     hipStream_t (NULL = the null stream); calls only enqueue work on it
+ *     and return -- the caller synchronises.  Every device buffer must stay alive until that work is
  *     done.  The nf4_layer array is host memory, copied into the workspace
  *     before the call returns; the caller may reuse it at once.
  *   - `ws` is caller-provided device scratch of at least the size the matching
@@ -71,6 +80,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP stream handle, declared as hip_runtime_api.h declares it, so that
+ * this header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
 
 #define NF4_ABI_VERSION 4
 
@@ -119,41 +132,54 @@ typedef struct {
 typedef struct {
     int64_t     n;        /* elements, 1 <= n < 2^40                                   */
     const void* w;        /* device [n] 16-bit weights, 16-byte aligned                */
-    uint8_t*    codes;    /* device [ceil(n/2)] packed codes, 4-byte aligned           */
+    uint8_t*    codes;    /* device [ceil(n/2)] packed codes, 16-byte aligned          */
     float*      absmax;   /* device [nb] exact fp32 block absmax, 4-byte aligned       */
     int8_t*     qabsmax;  /* device [nb] int8 double-quantised absmax                  */
     float*      scale2;   /* device [ng] fp32 second-level scales, 4-byte aligned      */
     void*       out;      /* device [n] 16-bit dequantised output, 16-byte aligned     */
 } nf4_layer;
 
-/* Blockwise NF4 quantisation of nl matrices in one grouped launch.
- * Reads w; writes codes and absmax; with dq_group == 256 also writes
- * qabsmax and scale2 (double quantisation fused into the same pass).
- * Required: w, codes, absmax; qabsmax and scale2 when dq_group == 256. */
+/* Blockwise NF4 quantisation of nl matrices in one grouped launch: the
+ * 4-bit NormalFloat codes and their per-block constants ("QLoRA" paper
+ * summary page, ai360xpert.com, How It Works, NF4 item; "QLoRA Explained",
+ * devtoolshub.net, NF4).  Reads w; writes codes and absmax; with
+ * dq_group == 256 also writes qabsmax and scale2 (double quantisation fused
+ * into the same pass).  Required: w, codes, absmax; qabsmax and scale2 when
+ * dq_group == 256.  ws: the descriptor table and an 8-byte record per
+ * 16,384-weight tile (nf4_workspace_bytes is enough). */
 nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
-                        void* ws, size_t ws_bytes, void* stream);
+                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Double quantisation of existing absmax constants (dq_group must be 256).
- * Reads absmax; writes qabsmax and scale2. */
+/* Double quantisation of existing absmax constants: the quantisation
+ * constants quantised again (QLoRA page, How It Works, Double Quantization
+ * item; "QLoRA Explained", Double Quantization); dq_group must be 256.
+ * Reads absmax; writes qabsmax and scale2.  ws: the descriptor table. */
 nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt,
-                            void* ws, size_t ws_bytes, void* stream);
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Dequantisation to the 16-bit type fmt.dtype.  Reads codes and either absmax
- * (dq_group == 0) or qabsmax + scale2 (dq_group == 256); writes out.
- * AQLoRA calls it for the layers that were not promoted.  ws: at least the
- * table and one 32-byte record per tile of these layers (nf4_workspace_bytes
- * of them, or of any superset, is enough). */
+/* Dequantisation to the 16-bit type fmt.dtype: the 4-bit weight turned back
+ * into 16 bits, as QLoRA does on the fly for the forward and backward pass
+ * (QLoRA page, How It Works) and as every non-promoted layer still needs
+ * under AQLoRA (AQLoRA paper listing, arxivdaily.com, English abstract).
+ * Reads codes and either absmax (dq_group == 0) or qabsmax + scale2
+ * (dq_group == 256); writes out.  ws: at least the table and one 32-byte
+ * record per tile of these layers (nf4_workspace_bytes of them, or of any
+ * superset, is enough). */
 nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
-                          void* ws, size_t ws_bytes, void* stream);
+                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The fused single pass: quantise (+ double-quantise), dequantise in
- * registers with the constants the user gets back, and score each matrix.
+ * registers with the constants the user gets back, and score each matrix by
+ * its NF4 reconstruction error -- AQLoRA's one pass over the weights, from
+ * the weights alone (AQLoRA listing, English abstract; "AQLoRA: A
+ * Zero-Search Recipe for Fast Quantized LoRA Fine-Tuning", aitrending.vip,
+ * Technical Details).
  * Reads w; writes codes, qabsmax and scale2 (dq_group == 256), absmax
  * (required when dq_group == 0, optional -- NULL skips it -- when 256), and
  * err[nl] (device fp64, the reconstruction error of each matrix).  out is not
  * touched. */
 nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
-                           double* err, void* ws, size_t ws_bytes, void* stream);
+                           double* err, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* nf4_layer_error without a workspace argument, for callers that cannot
  * allocate device memory (code that must not call hipMalloc: graph capture,
@@ -171,7 +197,7 @@ nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt,
  * (different streams, or host threads, without ordering between them) race
  * and give undefined results; calls ordered on one stream are safe. */
 nf4_status nf4_layer_error_noalloc(const nf4_layer* layers, int32_t nl, nf4_format fmt,
-                                   double* err, void* stream);
+                                   double* err, hipStream_t stream);
 /* Size in bytes of nf4_layer_error_noalloc's fixed per-device scratch. */
 size_t nf4_noalloc_scratch_bytes(void);
 
@@ -185,9 +211,12 @@ size_t nf4_noalloc_scratch_bytes(void);
  * aligned. */
 nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                                 double* err, double* sumsq, void* ws, size_t ws_bytes,
-                                void* stream);
+                                hipStream_t stream);
 
-/* Budgeted top-K over per-layer scores, on the device.
+/* Budgeted top-K over per-layer scores, on the device: rank the matrices by
+ * reconstruction error and keep the leading ones in 16 bits while the memory
+ * budget allows (AQLoRA listing, English abstract; aitrending page,
+ * Technical Details: the budget is a setting).
  *   err[nl]   device fp64 scores (finite, as written by nf4_layer_error)
  *   cost[nl]  device int64 promotion costs (aqlora_promote_cost)
  *   budget_bytes  < 0: no byte budget;  k_cap < 0: no count cap
@@ -197,7 +226,7 @@ nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format 
 nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl,
                               int64_t budget_bytes, int32_t k_cap,
                               uint8_t* selected, int32_t* k_out,
-                              void* ws, size_t ws_bytes, void* stream);
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Selection variants on the device.  The pages keep the top-K layers under a
  * memory budget, and their speed setting adapts only the top blocks
@@ -225,7 +254,7 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
                          int32_t nl, const int32_t* group_end, int32_t ngroups,
                          int64_t budget_bytes, int32_t k_cap, int32_t rule,
                          uint8_t* selected, int32_t* k_out,
-                         void* ws, size_t ws_bytes, void* stream);
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Codec variants ("QLoRA" paper summary page, How It Works, Double
  * Quantization item; "QLoRA Explained", Double Quantization: the constants
@@ -241,7 +270,7 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
  *   its absmax values in block order.
  * Codes use the exact absmax (the encode rule of the main codec with the block
  * size changed); y = RNE16(fl32(level[code] a')); err = sum (x - y)^2 (fp64).
- * layers: w (read, 16-byte aligned), codes (4-byte aligned), absmax (written:
+ * layers: w (read, 16-byte aligned), codes (16-byte aligned), absmax (written:
  * [ceil(n/block)] fp32), and for kinds 1-3 qabsmax (one byte per block: the
  * int8, or the E4M3 encoding) and scale2 ([ceil(nb/256)] fp32).  mean: device
  * fp32 [nl], written for kinds 2-3 (may be NULL otherwise).  err: device fp64
@@ -250,14 +279,14 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
  * second level + encode + dequantise + error). */
 nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
                                    float* mean, double* err, void* ws, size_t ws_bytes,
-                                   void* stream);
+                                   hipStream_t stream);
 
 /* Dequantisation of a variant's codes: reads codes, absmax (kind 0) or
  * qabsmax + scale2 (+ mean for kinds 2-3); writes out (16-byte aligned).
  * ws: at least the table and one 64-byte record per group of these layers
  * (nf4_workspace_bytes_variant of them, or of any superset, is enough). */
 nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
-                                  const float* mean, void* ws, size_t ws_bytes, void* stream);
+                                  const float* mean, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* NF4 dequantisation fused into the 16-bit matmul that consumes the weight,
  * on the matrix cores.  QLoRA dequantises the 4-bit weight on the fly for the
@@ -280,7 +309,7 @@ nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_varia
  * workspace; enqueues only.  Deterministic run to run. */
 nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                       int32_t backward, const void* x, int64_t m, void* out,
-                      int32_t out_fp32, void* stream);
+                      int32_t out_fp32, hipStream_t stream);
 
 /* nf4_matmul with a caller workspace, for shapes whose output tiles alone do
  * not fill the GPU (few tokens m): the reduction is then split into up to 16
@@ -299,7 +328,7 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
  * second kernel. */
 nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                          int32_t backward, const void* x, int64_t m, void* out,
-                         int32_t out_fp32, void* ws, size_t ws_bytes, void* stream);
+                         int32_t out_fp32, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- host-only helpers (pure; no HIP calls) ---- */
 
@@ -311,12 +340,12 @@ size_t      nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backw
 /* Workspace for every codec call above over these matrices (the descriptor
  * table, an 8-byte record per 16384-weight tile, and two arrays of 4 fp64
  * partials per tile); 0 on bad input. */
-size_t      nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format fmt);
+size_t      nf4_workspace_bytes(int32_t nl, const int64_t* n_per_layer, nf4_format fmt);
 /* Workspace for aqlora_select_topk and aqlora_select; 0 on bad input. */
 size_t      aqlora_workspace_bytes(int32_t nl);
 /* Workspace for the variant calls (the table, then the larger of two fp64 per
  * group and one 64-byte record per group); 0 on bad input. */
-size_t      nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_variant v);
+size_t      nf4_workspace_bytes_variant(int32_t nl, const int64_t* n_per_layer, nf4_variant v);
 /* ceil(n/2) + (kind 0 ? 4 nb : nb + 4 ng) + (kinds 2-3 ? 4 : 0); -1 on bad input. */
 int64_t     nf4_storage_bytes_variant(int64_t n, nf4_variant v);
 /* ceil(n/2) + (dq_group ? nb + 4*ng : 4*nb); -1 on bad input. */

@@ -96,14 +96,14 @@ EXPORTS = {
                                      ctypes.c_size_t, ctypes.c_void_p]),
     "nf4_matmul_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                                      ctypes.c_int64]),
-    "nf4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32, nf4_format]),
+    "nf4_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_void_p, nf4_format]),
     "nf4_layer_error_variant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_variant,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_size_t, ctypes.c_void_p]),
     "nf4_dequantize_variant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_variant,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                               ctypes.c_void_p]),
-    "nf4_workspace_bytes_variant": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32,
+    "nf4_workspace_bytes_variant": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_void_p,
                                                       nf4_variant]),
     "nf4_storage_bytes_variant": (ctypes.c_int64, [ctypes.c_int64, nf4_variant]),
     "aqlora_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
@@ -288,7 +288,7 @@ def nf4_dequantize_variant(layers, v: nf4_variant, ws, mean=None, stream=None) -
 
 def nf4_workspace_bytes_variant(ns, v: nf4_variant) -> int:
     a = np.ascontiguousarray(ns, np.int64)
-    return int(lib().nf4_workspace_bytes_variant(a.ctypes.data if a.size else None, a.size, v))
+    return int(lib().nf4_workspace_bytes_variant(a.size, a.ctypes.data if a.size else None, v))
 
 
 def nf4_storage_bytes_variant(n: int, v: nf4_variant) -> int:
@@ -299,7 +299,7 @@ def nf4_storage_bytes_variant(n: int, v: nf4_variant) -> int:
 
 def nf4_workspace_bytes(ns, f: nf4_format) -> int:
     a = np.ascontiguousarray(ns, np.int64)
-    return int(lib().nf4_workspace_bytes(a.ctypes.data, a.size, f))
+    return int(lib().nf4_workspace_bytes(a.size, a.ctypes.data, f))
 
 
 def aqlora_workspace_bytes(nl: int) -> int:
@@ -340,7 +340,7 @@ class LayerSet:
     """Device buffers for ``len(ns)`` matrices of ``ns[i]`` elements.
 
     Each buffer kind is one tensor; layer i's slice starts at an offset that
-    keeps the ABI's alignment (weights and outputs 16 B, codes 4 B).
+    keeps the ABI's alignment (weights, codes and outputs 16 B).
     Attributes: ``w`` (int16 bits), ``codes`` (uint8), ``absmax`` (float32),
     ``qabsmax`` (int8), ``scale2`` (float32), ``out`` (int16 bits), the offset
     lists ``*_off``, and ``c_layers`` (the nf4_layer array).  ``w``, ``codes``

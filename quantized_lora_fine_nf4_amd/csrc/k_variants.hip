@@ -48,9 +48,7 @@ constexpr int kVWaves = kVThreads / 64;
 constexpr int kVCells = 129;            // encode cells, trunc(64 s) in [-64, 64]
 constexpr int kVRepl = 16;              // lane-indexed copies of the cell table
 constexpr int kVYs = 256 + 17;          // dequant table stride (per code), padded against bank conflicts
-#ifndef NF4_VAR_HOLD
-#define NF4_VAR_HOLD 32                 // largest block size whose group stays in registers (kinds 0/1)
-#endif
+constexpr int kVarHold = 32;            // largest block size whose group stays in registers (kinds 0/1)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
@@ -469,7 +467,7 @@ __device__ __forceinline__ double encode_load(const VShared& sh, const u32x4 v, 
 
 template <int B>
 struct Held {
-    u32x4 v[(B <= NF4_VAR_HOLD) ? B / 8 : 1];
+    u32x4 v[(B <= kVarHold) ? B / 8 : 1];
 };
 
 template <int DT, int B, bool FULL, bool SPEC, bool HOLD, bool D32>
@@ -505,7 +503,7 @@ __device__ __forceinline__ void var_codec_body(VShared& sh, const VGroup& g, int
                                                const float* mean, double* partial)
 {
     constexpr bool FUSED = KIND <= 1;
-    constexpr bool HOLD = FUSED && B <= NF4_VAR_HOLD;
+    constexpr bool HOLD = FUSED && B <= kVarHold;
     constexpr int NL = B / 8;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const LayerDesc& d = *g.d;

@@ -57,7 +57,7 @@ nf4_status check_layers(const nf4_layer* L, int32_t nl, unsigned need, int64_t* 
         if ((need & NEED_S2) && !x.scale2) return NF4_E_ARG;
         if ((need & NEED_OUT) && !x.out) return NF4_E_ARG;
         if ((need & NEED_W) && !aligned(x.w, 16)) return NF4_E_ALIGN;
-        if ((need & NEED_CODES) && !aligned(x.codes, 4)) return NF4_E_ALIGN;
+        if ((need & NEED_CODES) && !aligned(x.codes, 16)) return NF4_E_ALIGN;
         if ((need & (NEED_ABSMAX | OPT_ABSMAX)) && x.absmax && !aligned(x.absmax, 4)) return NF4_E_ALIGN;
         if ((need & NEED_S2) && !aligned(x.scale2, 4)) return NF4_E_ALIGN;
         if ((need & NEED_OUT) && !aligned(x.out, 16)) return NF4_E_ALIGN;
@@ -159,7 +159,7 @@ int64_t variant_groups(const nf4_layer* L, int32_t nl, int block)
 // The fused pass; with sumsq also the per-layer sum of x^2 (partials for it
 // follow the error partials in the workspace).
 nf4_status layer_error_impl(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
-                            double* sumsq, void* ws, size_t ws_bytes, void* stream)
+                            double* sumsq, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     nf4_status st = check_format(fmt);
     if (st != NF4_OK) return st;
@@ -173,7 +173,7 @@ nf4_status layer_error_impl(const nf4_layer* layers, int32_t nl, nf4_format fmt,
     if (!aligned(err, 8) || (sumsq && !aligned(sumsq, 8))) return NF4_E_ALIGN;
     const size_t need = table_bytes(nl) + record_bytes(ntiles) + (sumsq ? 2 : 1) * partial_bytes(ntiles);
     if ((st = check_ws(ws, ws_bytes, need)) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     const LayerDesc* tab = static_cast<const LayerDesc*>(ws);
     char* rec = static_cast<char*>(ws) + table_bytes(nl);
@@ -229,13 +229,13 @@ nf4_status check_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_form
 
 nf4_status run_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt, int32_t backward,
                       const void* x, int64_t m, void* out, int32_t out_fp32, float* part, int nsplit,
-                      void* stream)
+                      hipStream_t stream)
 {
     const bool dq = fmt.dq_group != 0;
     hipError_t e = nf4k::launch_nf4_matmul(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
                                            dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax,
                                            rows, cols, backward == 0, x, m, out, out_fp32 == 1,
-                                           part, nsplit, static_cast<hipStream_t>(stream));
+                                           part, nsplit, stream);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
@@ -291,7 +291,7 @@ int64_t aqlora_promote_cost(int64_t n, nf4_format f)
     return s < 0 ? -1 : 2 * n - s;
 }
 
-size_t nf4_workspace_bytes(const int64_t* n_per_layer, int32_t nl, nf4_format f)
+size_t nf4_workspace_bytes(int32_t nl, const int64_t* n_per_layer, nf4_format f)
 {
     if (!n_per_layer || nl <= 0 || nl > kMaxLayers || check_format(f) != NF4_OK) return 0;
     int64_t ntiles = 0;
@@ -311,7 +311,7 @@ size_t aqlora_workspace_bytes(int32_t nl)
 }
 
 nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
-                        size_t ws_bytes, void* stream)
+                        size_t ws_bytes, hipStream_t stream)
 {
     nf4_status st = check_format(fmt);
     if (st != NF4_OK) return st;
@@ -321,7 +321,7 @@ nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, voi
                       &ntiles);
     if (st != NF4_OK) return st;
     if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + record_bytes(ntiles))) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_codec(static_cast<const LayerDesc*>(ws), nl, ntiles,
                                       any_ragged(layers, nl), fmt.dtype, dq,
@@ -330,7 +330,7 @@ nf4_status nf4_quantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, voi
 }
 
 nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
-                            size_t ws_bytes, void* stream)
+                            size_t ws_bytes, hipStream_t stream)
 {
     nf4_status st = check_format(fmt);
     if (st != NF4_OK) return st;
@@ -339,14 +339,14 @@ nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt,
     st = check_layers(layers, nl, NEED_ABSMAX | NEED_Q | NEED_S2, &ntiles);
     if (st != NF4_OK) return st;
     if ((st = check_ws(ws, ws_bytes, table_bytes(nl))) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_double_quant(static_cast<const LayerDesc*>(ws), nl, ntiles, s);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
 nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
-                          size_t ws_bytes, void* stream)
+                          size_t ws_bytes, hipStream_t stream)
 {
     nf4_status st = check_format(fmt);
     if (st != NF4_OK) return st;
@@ -357,7 +357,7 @@ nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, v
     if (st != NF4_OK) return st;
     // the table, then one 32-byte record per tile (where the fused pass keeps its partials)
     if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + partial_bytes(ntiles))) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_dequant(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype,
                                         dq, static_cast<char*>(ws) + table_bytes(nl), s);
@@ -365,13 +365,13 @@ nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, v
 }
 
 nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
-                           void* ws, size_t ws_bytes, void* stream)
+                           void* ws, size_t ws_bytes, hipStream_t stream)
 {
     return layer_error_impl(layers, nl, fmt, err, nullptr, ws, ws_bytes, stream);
 }
 
 nf4_status nf4_layer_error_noalloc(const nf4_layer* layers, int32_t nl, nf4_format fmt,
-                                   double* err, void* stream)
+                                   double* err, hipStream_t stream)
 {
     // the same checks as nf4_layer_error, then the size check against the
     // fixed scratch, all before anything is looked up or enqueued
@@ -396,7 +396,7 @@ nf4_status nf4_layer_error_noalloc(const nf4_layer* layers, int32_t nl, nf4_form
 size_t nf4_noalloc_scratch_bytes(void) { return nf4k::kScratchBytes; }
 
 nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,
-                                double* sumsq, void* ws, size_t ws_bytes, void* stream)
+                                double* sumsq, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (!sumsq) return NF4_E_ARG;
     return layer_error_impl(layers, nl, fmt, err, sumsq, ws, ws_bytes, stream);
@@ -404,7 +404,7 @@ nf4_status nf4_layer_error_norm(const nf4_layer* layers, int32_t nl, nf4_format 
 
 nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl,
                               int64_t budget_bytes, int32_t k_cap, uint8_t* selected,
-                              int32_t* k_out, void* ws, size_t ws_bytes, void* stream)
+                              int32_t* k_out, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (!err || !cost || !selected || !k_out) return NF4_E_ARG;
     if (nl <= 0 || nl > kMaxSelectLayers) return NF4_E_ARG;
@@ -415,14 +415,14 @@ nf4_status aqlora_select_topk(const double* err, const int64_t* cost, int32_t nl
     int32_t* perm = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                align256(size_t(nl) * sizeof(int32_t)));
     hipError_t e = nf4k::launch_select(err, cost, nl, budget_bytes, k_cap, selected, k_out, rank,
-                                       perm, static_cast<hipStream_t>(stream));
+                                       perm, stream);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
 nf4_status aqlora_select(const double* err, const double* denom, const int64_t* cost, int32_t nl,
                          const int32_t* group_end, int32_t ngroups, int64_t budget_bytes,
                          int32_t k_cap, int32_t rule, uint8_t* selected, int32_t* k_out,
-                         void* ws, size_t ws_bytes, void* stream)
+                         void* ws, size_t ws_bytes, hipStream_t stream)
 {
     if (!err || !cost || !selected || !k_out) return NF4_E_ARG;
     if (nl <= 0 || nl > kMaxSelectLayers) return NF4_E_ARG;
@@ -441,7 +441,7 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
     nf4_status st = check_ws(ws, ws_bytes, L.total);
     if (st != NF4_OK) return st;
     char* w = static_cast<char*>(ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     int32_t* ge = nullptr;
     if (group_end) {
         // pageable source: staged by the runtime before the call returns
@@ -463,7 +463,7 @@ nf4_status aqlora_select(const double* err, const double* denom, const int64_t* 
 
 nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                       int32_t backward, const void* x, int64_t m, void* out, int32_t out_fp32,
-                      void* stream)
+                      hipStream_t stream)
 {
     nf4_status st = check_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32);
     if (st != NF4_OK) return st;
@@ -482,7 +482,7 @@ size_t nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, 
 
 nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                          int32_t backward, const void* x, int64_t m, void* out, int32_t out_fp32,
-                         void* ws, size_t ws_bytes, void* stream)
+                         void* ws, size_t ws_bytes, hipStream_t stream)
 {
     nf4_status st = check_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32);
     if (st != NF4_OK) return st;
@@ -494,7 +494,7 @@ nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_for
         hipError_t e = nf4k::launch_nf4_gemv(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
                                              dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax, rows, cols,
                                              x, m, out, out_fp32 == 1, static_cast<float*>(ws), gv,
-                                             static_cast<hipStream_t>(stream));
+                                             stream);
         return e == hipSuccess ? NF4_OK : hip_fail(e);
     }
     const int nsplit = nf4k::nf4_matmul_splits(rows, cols, backward == 0, m);
@@ -507,7 +507,7 @@ nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_for
                       stream);
 }
 
-size_t nf4_workspace_bytes_variant(const int64_t* n_per_layer, int32_t nl, nf4_variant v)
+size_t nf4_workspace_bytes_variant(int32_t nl, const int64_t* n_per_layer, nf4_variant v)
 {
     if (!n_per_layer || nl <= 0 || nl > kMaxLayers || check_variant(v) != NF4_OK) return 0;
     int64_t g = 0;
@@ -529,7 +529,7 @@ int64_t nf4_storage_bytes_variant(int64_t n, nf4_variant v)
 
 nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
                                    float* mean, double* err, void* ws, size_t ws_bytes,
-                                   void* stream)
+                                   hipStream_t stream)
 {
     nf4_status st = check_variant(v);
     if (st != NF4_OK) return st;
@@ -544,7 +544,7 @@ nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_vari
     const int64_t ng = variant_groups(layers, nl, v.blocksize);
     const size_t part = align256(size_t(ng) * sizeof(double));
     if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + 2 * part)) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     if ((st = stage_table_variant(layers, nl, v.blocksize, ws, s)) != NF4_OK) return st;
     char* w = static_cast<char*>(ws);
     hipError_t e = nf4k::launch_variant_error(
@@ -555,7 +555,7 @@ nf4_status nf4_layer_error_variant(const nf4_layer* layers, int32_t nl, nf4_vari
 }
 
 nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_variant v,
-                                  const float* mean, void* ws, size_t ws_bytes, void* stream)
+                                  const float* mean, void* ws, size_t ws_bytes, hipStream_t stream)
 {
     nf4_status st = check_variant(v);
     if (st != NF4_OK) return st;
@@ -568,7 +568,7 @@ nf4_status nf4_dequantize_variant(const nf4_layer* layers, int32_t nl, nf4_varia
     if (with_mean && !aligned(mean, 4)) return NF4_E_ALIGN;
     const int64_t ng = variant_groups(layers, nl, v.blocksize);
     if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + align256(size_t(ng) * 64))) != NF4_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = stream;
     if ((st = stage_table_variant(layers, nl, v.blocksize, ws, s)) != NF4_OK) return st;
     hipError_t e = nf4k::launch_variant_dequant(static_cast<const LayerDesc*>(ws), nl, ng, v.dtype,
                                                 v.blocksize, v.dq_kind, with_mean ? mean : nullptr,

@@ -139,12 +139,12 @@ def test_tile_count_limit(name):
 @pytest.mark.parametrize("name", CODEC)
 def test_misaligned_pointers(name):
     f = q.fmt()
-    fields = {"nf4_quantize": {"w": 16, "codes": 4, "absmax": 4, "scale2": 4},
+    fields = {"nf4_quantize": {"w": 16, "codes": 16, "absmax": 4, "scale2": 4},
               "nf4_double_quant": {"absmax": 4, "scale2": 4},
-              "nf4_dequantize": {"codes": 4, "scale2": 4, "out": 16},
-              "nf4_layer_error": {"w": 16, "codes": 4, "absmax": 4, "scale2": 4}}[name]
+              "nf4_dequantize": {"codes": 16, "scale2": 4, "out": 16},
+              "nf4_layer_error": {"w": 16, "codes": 16, "absmax": 4, "scale2": 4}}[name]
     for field, a in fields.items():
-        for off in (1, 2, a // 2) if a > 2 else (1,):
+        for off in (1, 2, 4, a // 2) if a > 2 else (1,):
             if off % a:
                 assert _call(name, [_L(**{field: FAKE + off})], f) == q.NF4_E_ALIGN, (field, off)
 
