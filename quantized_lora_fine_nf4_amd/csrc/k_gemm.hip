@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "nf4_format.h"
 #include "nf4_internal.h"
 #include "nf4_launch.h"
@@ -130,6 +132,7 @@ struct GemmArgs {
     int64_t tile0;          // first (tile, split) index of this launch
     int64_t ntiles;         // output tiles (row tiles x column tiles)
     int nsplit;             // splits of the reduction (1: none)
+    int64_t nfull, nhalf;   // 256 x 256 forward tiles: whole tiles, then tiles split in two halves (0: none)
     int split_steps;        // k-steps per split
     float* part;            // nsplit > 1: fp32 partials [nsplit][M x ncol]
 };
@@ -391,6 +394,320 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
             }
 }
 
+// ---- large m, forward: 256 x 256 output tiles, the weight operand
+// dequantised straight into matrix-core registers
+//
+// Four waves side by side: wave w owns output columns (W rows) c0 + 64 w ..
+// c0 + 64 w + 63 (two 32-column MFMA tiles) over all 256 rows of the x tile
+// (eight 32-row tiles), so each weight is dequantised once per workgroup and
+// never stored anywhere.  A 64-wide k-step is one quantisation block of every
+// W row: lane (q, h) = (l % 32, l / 32) loads the 32 codes of W row
+// c0 + 64 w + 32 j + q at k 32 h .. 32 h + 31 (one 16-byte load) and MFMA kk of
+// the step takes k 32 h + 8 kk .. + 7 of them; the x fragment reads the same k
+// from LDS, so the two operands agree (the order of the reduction inside a
+// step is not W's storage order, which only reorders the fp32 sum).  x is
+// staged through two LDS buffers, one barrier per step; the next step's x rows
+// and codes are loaded while this one multiplies.  Levels come from a table of
+// level pairs per code byte in 32 interleaved copies, lane l reading copy
+// l % 32 so that any codes hit distinct banks: entry e of copy c sits at byte
+// 256 e + 8 c, an address one byte permute builds from the code byte.
+constexpr int kXM = 256, kXN = 256;           // output tile: x rows, output columns
+constexpr int kXPitch = 72;                   // staged x row, 16-bit elements (144 B: conflict-free 16-B reads)
+constexpr int kLutCopies = 32;
+constexpr int kLutBytes = 256 * kLutCopies * 8;
+constexpr int kXBuf = kXM * kXPitch * 2;      // bytes per x buffer
+constexpr int kXLds = kLutBytes + 2 * kXBuf;  // 139,264 B of LDS: one workgroup per CU
+
+// Tile t of a launch of n workgroups in an order where each XCD (workgroups
+// are dealt to the eight XCDs in turn) takes a contiguous run of tiles.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n)
+{
+    const int64_t per = n >> 3, rem = n & 7, x = b & 7, i = b >> 3;
+    return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+// Output tile coordinates in groups of four row tiles, column tiles outer.
+__device__ __forceinline__ void group_coords(int64_t tile, int64_t mtiles, int64_t ntn, int64_t& mt, int64_t& nt)
+{
+    constexpr int kG = 4;
+    const int64_t per = kG * ntn, first = (tile / per) * kG;
+    const int64_t gsz = mtiles - first < kG ? mtiles - first : kG;
+    const int64_t in = tile % per;
+    mt = first + in % gsz;
+    nt = in / gsz;
+}
+
+// Eight codes (one dword, element 2j in the low nibble of byte j) to eight
+// 16-bit values through the level-pair table; lb = this lane's copy offset.
+template <int DT>
+__device__ __forceinline__ u32x4 deq8_pairs(uint32_t c, float adq, const uint8_t* lut, uint32_t lb)
+{
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // byte 1 <- code byte j, byte 0 <- lb, bytes 3:2 <- lb's zero byte 2
+        const uint32_t addr = __builtin_amdgcn_perm(c, lb, 0x02020000u | ((4u + j) << 8));
+        const f2 p = *(const f2*)(lut + addr);
+        r[j] = pack16<DT>(p.x * adq, p.y * adq);
+    }
+    return r;
+}
+
+// One output tile of MT * 32 x rows (MT = 8: a whole 256-row tile; 4: one
+// half of it) and 256 output columns, over k-steps step0 .. step0 + nsteps - 1,
+// into out (or the fp32 partials of split `split`).  s_mem holds the level
+// table; the x buffers follow it.
+template <int DT, bool DQ, bool OUT_F32, bool PART, int MT>
+__device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, q = lane & 31, h = lane >> 5;
+    const uint8_t* lut = s_mem;
+    const uint32_t lb = (uint32_t)q << 3;
+    const bool live = c0 + 64 * wv < g.ncol;   // wave-uniform: a 128-column tail leaves waves 2, 3 idle
+    const int ksteps = (int)(g.kred / 64);
+    const int step0 = PART ? split * g.split_steps : 0;
+    const int nsteps = PART ? min(g.split_steps, ksteps - step0) : ksteps;
+
+    // Loads address a uniform base (scalar registers, advanced per step) plus
+    // a 32-bit lane offset; the launcher keeps 256 rows of x and of the codes
+    // under 2 GiB.  x: thread t stages rows (t >> 3) + 32 i, 16-byte chunk
+    // t & 7; rows past M repeat row M - 1 (they feed only output rows that are
+    // not stored).
+    const GLOBAL uint8_t* xb = (const GLOBAL uint8_t*)((const GLOBAL uint16_t*)g.a + m0 * g.lda + (int64_t)step0 * 64);
+    uint32_t xo[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        int64_t row = m0 + (t >> 3) + 32 * i;
+        row = row < g.M ? row : g.M - 1;
+        xo[i] = (uint32_t)(((row - m0) * g.lda + 8 * (t & 7)) * 2);
+    }
+    // W rows of this lane: n_j = c0 + 64 wv + 32 j + q (in bounds when live)
+    const int64_t nrow0 = c0 + 64 * wv + q;
+    const int64_t bpr = g.cols / 64;   // blocks per W row
+    const int64_t wrow = c0 + 64 * (int64_t)__builtin_amdgcn_readfirstlane(wv);   // wave-uniform
+    const GLOBAL uint8_t* cb = (const GLOBAL uint8_t*)g.codes + ((wrow * g.cols + (int64_t)step0 * 64) >> 1);
+    const int64_t kb = wrow * bpr + step0;   // block of W row wrow at the first step
+    uint32_t co[2], ko[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        co[j] = (uint32_t)((((32 * j + q) * g.cols) >> 1) + 16 * h);
+        ko[j] = (uint32_t)((32 * j + q) * bpr);
+    }
+    // buffer resources over the uniform bases: the step offset goes in the
+    // scalar offset, the lane offset in the vector offset (no per-step vector
+    // address arithmetic); 0x00020000 selects raw 32-bit data
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t cs = __builtin_amdgcn_make_buffer_rsrc((void*)cb, 0, 0x7fffffff, 0x00020000);
+    const void* kbase = DQ ? (const void*)((const int8_t*)g.qabsmax + kb) : (const void*)((const float*)g.absmax + kb);
+    const __amdgpu_buffer_rsrc_t ks = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ss =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(DQ ? g.scale2 : g.absmax), 0, 0x7fffffff, 0x00020000);
+    auto ld_x = [&](int i, int s) { return __builtin_amdgcn_raw_buffer_load_b128(xs, xo[i], 128 * s, 0); };
+    auto ld_c = [&](int j, int s) { return __builtin_amdgcn_raw_buffer_load_b128(cs, co[j], 32 * s, 0); };
+    // constants of this lane's rows at step s (relative to step0); the scale
+    // of block b is scale2[b >> 8], b = kb + s + ko[j] = 256 A + (B + ko[j])
+    auto ld_k = [&](int j, int s) -> RawConst {
+        if constexpr (DQ) {
+            const int8_t qv = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(ks, ko[j], s, 0);
+            const int64_t kbs = kb + s;
+            const uint32_t grp = (uint32_t)(kbs & 255) + ko[j];
+            const float sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                 ss, (grp >> 8) << 2, (int)((kbs >> 8) << 2), 0));
+            return RawConst{qv, sv};
+        } else {
+            return RawConst{0, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ks, ko[j] << 2, 4 * s, 0))};
+        }
+    };
+
+    f32x16 acc[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    u32x4 xr[MT], cw[2], cn[2];
+    RawConst kc[2], kn[2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, 0);
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            cw[j] = ld_c(j, 0);
+            kc[j] = ld_k(j, 0);
+        }
+    }
+    uint16_t* xs0 = (uint16_t*)(s_mem + kLutBytes);
+    const int wofs = ((t >> 3)) * kXPitch + 8 * (t & 7);   // this thread's staging slot, row (t >> 3)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) *(u32x4*)(xs0 + wofs + 32 * i * kXPitch) = xr[i];
+    __syncthreads();   // level table and the first x tile
+
+    typedef typename Frag8<DT>::T F;
+    if (!live) {
+        // idle columns: stage x and keep the barriers in step with the others
+        for (int s = 0; s + 1 < nsteps; ++s) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, s + 1);
+            uint16_t* Xn = (uint16_t*)(s_mem + kLutBytes + ((s + 1) & 1) * kXBuf);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) *(u32x4*)(Xn + wofs + 32 * i * kXPitch) = xr[i];
+            __syncthreads();
+        }
+        return;
+    }
+    // Software pipeline over sub-steps kk of 16 MFMAs: while kk multiplies, the
+    // x fragments of kk + 1 are read, the level pairs of kk + 2 are looked up
+    // and the weight fragments of kk + 1 are finished from the pairs looked up
+    // one sub-step earlier (across the step boundary for the next step's
+    // codes).  Each sub-step is one scheduling region whose reads and ALU work
+    // are spread between its MFMAs.
+    F fa[2][MT], fb[2][2];
+    f2 lv[2][2][4];   // level pairs [slot][W tile j][code byte]
+    auto rd_x = [&](const uint16_t* X, int kk, F (&d)[MT]) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) d[i] = *(const F*)(X + (32 * i + q) * kXPitch + 32 * h + 8 * kk);
+    };
+    auto rd_lv = [&](const u32x4 (&c)[2], int kk, f2 (&d)[2][4]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)   // byte 1 <- code byte b, byte 0 <- lb, bytes 3:2 <- lb's zero byte 2
+                d[j][b] = *(const f2*)(lut + __builtin_amdgcn_perm(c[j][kk], lb, 0x02020000u | ((4u + b) << 8)));
+    };
+    auto mk_w = [&](const f2 (&p)[2][4], float a0, float a1, F (&d)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float a = j ? a1 : a0;
+            u32x4 r;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) r[b] = pack16<DT>(p[j][b].x * a, p[j][b].y * a);
+            d[j] = __builtin_bit_cast(F, r);
+        }
+    };
+    auto mm = [&](const F (&a)[MT], const F (&b)[2]) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            acc[i][0] = mfma32<DT>(a[i], b[0], acc[i][0]);
+            acc[i][1] = mfma32<DT>(a[i], b[1], acc[i][1]);
+        }
+    };
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, MT == 8 ? 1 : 2, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, MT == 8 ? 2 : 4, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    float a0 = block_const<DQ>(kc[0]), a1 = block_const<DQ>(kc[1]);
+    rd_lv(cw, 0, lv[0]);
+    mk_w(lv[0], a0, a1, fb[0]);
+    rd_lv(cw, 1, lv[1]);
+    for (int s = 0; s < nsteps; ++s) {
+        // the next step's codes, constants and x rows; the last step loads its
+        // own again (in bounds, and what the look-ahead computes from them is
+        // not used), which keeps the loop free of branches
+        const int sn = s + 1 < nsteps ? s + 1 : s;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            cn[j] = ld_c(j, sn);
+            kn[j] = ld_k(j, sn);
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, sn);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint16_t* X = (const uint16_t*)(s_mem + kLutBytes + (s & 1) * kXBuf);
+        rd_x(X, 0, fa[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(fa[0], fb[0]); rd_x(X, 1, fa[1]); rd_lv(cw, 2, lv[0]); mk_w(lv[1], a0, a1, fb[1]);
+        interleave();
+        mm(fa[1], fb[1]); rd_x(X, 2, fa[0]); rd_lv(cw, 3, lv[1]); mk_w(lv[0], a0, a1, fb[0]);
+        interleave();
+        const float n0 = block_const<DQ>(kn[0]), n1 = block_const<DQ>(kn[1]);
+        mm(fa[0], fb[0]); rd_x(X, 3, fa[1]); rd_lv(cn, 0, lv[0]); mk_w(lv[1], a0, a1, fb[1]);
+        interleave();
+        mm(fa[1], fb[1]); rd_lv(cn, 1, lv[1]); mk_w(lv[0], n0, n1, fb[0]);
+        interleave();
+        {   // the last step writes the other buffer too: nothing reads it again
+            uint16_t* Xn = (uint16_t*)(s_mem + kLutBytes + ((s + 1) & 1) * kXBuf);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) *(u32x4*)(Xn + wofs + 32 * i * kXPitch) = xr[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) { cw[j] = cn[j]; kc[j] = kn[j]; }
+        a0 = n0;
+        a1 = n1;
+        __syncthreads();
+    }
+
+    // D layout of a 32 x 32 tile: lane l, value r -> row 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column l % 32
+    const bool full = m0 + 32 * MT <= g.M;
+    const int64_t rbase = m0 + 4 * h;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+                const int64_t col = nrow0 + 32 * j;
+                if (full || row < g.M) {
+                    if constexpr (PART)
+                        ((GLOBAL float*)g.part)[(int64_t)split * g.M * g.ldo + row * g.ldo + col] = acc[i][j][r];
+                    else if constexpr (OUT_F32)
+                        ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
+                    else
+                        ((GLOBAL uint16_t*)g.out)[row * g.ldo + col] = (uint16_t)pack16<DT>(acc[i][j][r], 0.0f);
+                }
+            }
+}
+
+
+// The launch order: with nhalf > 0 it holds nfull whole tiles, then nhalf
+// tiles each split in two halves of 128 x rows (the tiles left over after the
+// whole rounds of one workgroup per CU: splitting them shortens the last
+// round); every XCD takes its share of whole tiles first and then its share of
+// halves, both contiguous in the tile order.
+template <int DT, bool DQ, bool OUT_F32, bool PART>
+__global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[kXLds];
+    const int t = threadIdx.x;
+    {
+        // thread t builds entry t; the copy pairs are written in a rotated
+        // order so that the lanes of one write hit distinct banks
+        const uint32_t lo = __builtin_bit_cast(uint32_t, level_imm(t & 15));
+        const uint32_t hi = __builtin_bit_cast(uint32_t, level_imm(t >> 4));
+        u32x4* row = (u32x4*)(s_mem + 256 * t);
+#pragma unroll
+        for (int c = 0; c < kLutCopies / 2; ++c) row[(c + t) & (kLutCopies / 2 - 1)] = u32x4{lo, hi, lo, hi};
+    }
+    int64_t tile;
+    int half = -1;
+    if (g.nhalf == 0) {
+        tile = g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
+    } else {
+        const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3, hpx = g.nhalf >> 2;
+        if (i < fpx) {
+            tile = x * fpx + i;
+        } else {
+            const int64_t hh = x * hpx + (i - fpx);
+            tile = g.nfull + (hh >> 1);
+            half = (int)(hh & 1);
+        }
+    }
+    const int split = PART ? (int)(tile / g.ntiles) : 0;
+    if (PART) tile -= (int64_t)split * g.ntiles;
+    int64_t mt, nt;
+    group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
+    if (half < 0) mm_fwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
+    else mm_fwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * half, nt * kXN, split);
+}
+
 // ---- few tokens, forward: one wave per 16 W rows and one part of the reduction
 //
 // out[m x rows] = x[m x cols] W^T for m <= 32 on v_mfma_f32_16x16x32 (x rows
@@ -546,9 +863,70 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float* __restrict__ pa
 // One-shot launches of at most 2^32 / 256 - 1 workgroups each.
 constexpr int64_t kMaxGemmGrid = (int64_t(1) << 32) / kGThreads - 1;
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+template <int DT, bool DQ, bool OUT_F32>
+hipError_t mm_fwd_go(GemmArgs g, hipStream_t s)
+{
+    g.ntn = (g.ncol + kXN - 1) / kXN;
+    g.ntiles = ((g.M + kXM - 1) / kXM) * g.ntn;
+    const int64_t total = g.ntiles * g.nsplit;
+    // With one workgroup per CU, the tiles past the last whole round run as
+    // halves when those fit one round and the split is even across XCDs.
+    g.nfull = total;
+    g.nhalf = 0;
+    const int64_t ncu = cu_count();
+    if (g.nsplit == 1 && ncu > 0 && total > ncu && total + ncu < kMaxGemmGrid) {
+        const int64_t rem = total % ncu, full = total - rem;
+        if (rem > 0 && 2 * rem <= ncu && full % 8 == 0 && rem % 4 == 0) {
+            g.nfull = full;
+            g.nhalf = rem;
+            g.tile0 = 0;
+            hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, false>), dim3((unsigned)(full + 2 * rem)), dim3(256),
+                               0, s, g);
+            return hipGetLastError();
+        }
+    }
+    for (int64_t t0 = 0; t0 < total; t0 += kMaxGemmGrid) {
+        const int64_t n = total - t0 < kMaxGemmGrid ? total - t0 : kMaxGemmGrid;
+        g.tile0 = t0;
+        if (g.nsplit > 1)
+            hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, true>), dim3((unsigned)n), dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, false>), dim3((unsigned)n), dim3(256), 0, s, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (g.nsplit > 1) {
+        const int64_t n = g.M * g.ncol;
+        const int64_t blocks = (n / 4 + 255) / 256;
+        if (blocks > kMaxGemmGrid) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_splitk_sum<DT, OUT_F32>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           (const float*)g.part, g.nsplit, n, g.out);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
 template <int DT, bool FWD, bool DQ, bool OUT_F32>
 hipError_t gemm_go(GemmArgs g, hipStream_t s)
 {
+    if constexpr (FWD) {
+        // 32-bit lane offsets: 256 rows of x (and of codes) under 2 GiB
+        if (g.nsplit <= 1 && g.M > 128 && g.kred < (int64_t(1) << 22)) return mm_fwd_go<DT, DQ, OUT_F32>(g, s);
+    }
     const int64_t total = g.ntiles * g.nsplit;
     for (int64_t t0 = 0; t0 < total; t0 += kMaxGemmGrid) {
         const int64_t n = total - t0 < kMaxGemmGrid ? total - t0 : kMaxGemmGrid;
@@ -688,6 +1066,8 @@ hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabs
     g.ntn = g.ncol / kBN;
     g.tile0 = 0;
     g.ntiles = ((m + kBM - 1) / kBM) * g.ntn;
+    g.nfull = g.ntiles;
+    g.nhalf = 0;
     const int ksteps = (int)(g.kred / kBK);
     g.nsplit = (part && nsplit > 1) ? nsplit : 1;
     g.split_steps = (ksteps + g.nsplit - 1) / g.nsplit;
