@@ -546,10 +546,10 @@ __device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, i
 
     typedef typename Frag8<DT>::T F;
     if (!live) {
-        // idle columns: stage x and keep the barriers in step with the others
-        for (int s = 0; s + 1 < nsteps; ++s) {
+        // idle columns: stage x as the live waves do, barrier for barrier
+        for (int s = 0; s < nsteps; ++s) {
 #pragma unroll
-            for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, s + 1);
+            for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, s + 1 < nsteps ? s + 1 : s);
             uint16_t* Xn = (uint16_t*)(s_mem + kLutBytes + ((s + 1) & 1) * kXBuf);
 #pragma unroll
             for (int i = 0; i < MT; ++i) *(u32x4*)(Xn + wofs + 32 * i * kXPitch) = xr[i];
@@ -706,6 +706,281 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
     group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
     if (half < 0) mm_fwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
     else mm_fwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * half, nt * kXN, split);
+}
+
+// ---- large m, backward (input gradient): 256 x 256 output tiles, the weight
+// transposed through LDS
+//
+// out[m, c] = sum_n x[m, n] W[n, c]: the reduction runs over W's rows, across
+// its quantisation blocks, so an MFMA weight fragment (eight consecutive n of
+// one column) is not contiguous in W.  Wave w owns output columns
+// c0 + 64 w .. + 63 over all 256 rows of the x tile.  For each 64-row k-step
+// it dequantises its own 64 x 64 piece of W, lane l taking W row n0 + l
+// (exactly one block: 32 code bytes and one constant), writes it to a private
+// LDS region in W's order, and reads its weight fragments back with the
+// transposing 64-bit LDS read: in each group of 16 lanes, lane i receives
+// element i % 4 of the 4-element pieces read by lanes 4 k + i / 4 (k = 0..3),
+// so the 16 lanes reading rows r .. r + 3 at columns C + 4 (i % 4) come back
+// as column C + i, rows r .. r + 3.  The step's dequantisation runs one step
+// ahead of its MFMAs, spread over the four sub-steps; x is double-buffered as
+// in the forward kernel.  Region rows are 128 B with chunk c of row r at slot
+// c ^ (2 (r % 4) + (r / 4) % 2), conflict-free for both the row writes and
+// the transposing reads; x rows are 128 B with chunk c of row r at c ^ (r % 8).
+constexpr int kBXBuf = 256 * 128;                   // x buffer: 256 rows x 64 16-bit values
+constexpr int kBWReg = 64 * 128;                    // per-wave W region: 64 rows x 64 16-bit values
+constexpr int kBLds = kLutBytes + 2 * kBXBuf + 4 * kBWReg;   // 163,840 B
+static_assert(kBLds <= 163840, "LDS of one CU");
+
+__device__ __forceinline__ int wslot(int r, int c) { return c ^ (((r & 3) << 1) | ((r >> 2) & 1)); }
+
+template <int DT, bool DQ, bool OUT_F32, bool PART, int MT>
+__device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, q = lane & 31, h = lane >> 5;
+    const uint8_t* lut = s_mem;
+    const uint32_t lb = (uint32_t)q << 3;
+    const bool live = c0 + 64 * wv < g.ncol;   // wave-uniform
+    const int ksteps = (int)(g.kred / 64);
+    const int step0 = PART ? split * g.split_steps : 0;
+    const int nsteps = PART ? min(g.split_steps, ksteps - step0) : ksteps;
+
+    // x (the output gradient, M x rows): thread t stages rows (t >> 3) + 32 i,
+    // chunk t & 7; rows past M repeat row M - 1.  Loads: uniform base, step in
+    // the scalar offset, 32-bit lane offset (the launcher keeps them in range).
+    const GLOBAL uint8_t* xb = (const GLOBAL uint8_t*)((const GLOBAL uint16_t*)g.a + m0 * g.lda + (int64_t)step0 * 64);
+    uint32_t xo[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        int64_t row = m0 + (t >> 3) + 32 * i;
+        row = row < g.M ? row : g.M - 1;
+        xo[i] = (uint32_t)(((row - m0) * g.lda + 8 * (t & 7)) * 2);
+    }
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, 0, 0x7fffffff, 0x00020000);
+    // W: lane l dequantises row n0 + l, columns cw .. cw + 63 (block cw / 64)
+    const int64_t cw = c0 + 64 * (int64_t)__builtin_amdgcn_readfirstlane(wv);   // wave-uniform
+    const int64_t bpr = g.cols / 64;
+    const GLOBAL uint8_t* cb = (const GLOBAL uint8_t*)g.codes + (((int64_t)step0 * 64 * g.cols + cw) >> 1);
+    const __amdgpu_buffer_rsrc_t cs = __builtin_amdgcn_make_buffer_rsrc((void*)cb, 0, 0x7fffffff, 0x00020000);
+    const uint32_t co = (uint32_t)(lane * (g.cols >> 1));
+    const int64_t kb = (int64_t)step0 * 64 * bpr + (cw >> 6);   // block of row n0, columns cw.. at the first step
+    const uint32_t ko = (uint32_t)(lane * bpr);
+    const void* kbase = DQ ? (const void*)((const int8_t*)g.qabsmax + kb) : (const void*)((const float*)g.absmax + kb);
+    const __amdgpu_buffer_rsrc_t ks = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ss =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(DQ ? g.scale2 : g.absmax), 0, 0x7fffffff, 0x00020000);
+    const int32_t cstep = (int32_t)(32 * g.cols);   // code bytes per k-step
+    const int32_t kstep = (int32_t)(64 * bpr);      // blocks per k-step
+    auto ld_x = [&](int i, int s) { return __builtin_amdgcn_raw_buffer_load_b128(xs, xo[i], 128 * s, 0); };
+    auto ld_c = [&](int half, int s) { return __builtin_amdgcn_raw_buffer_load_b128(cs, co + 16 * half, cstep * s, 0); };
+    auto ld_k = [&](int s) -> RawConst {
+        if constexpr (DQ) {
+            const int8_t qv = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(ks, ko, kstep * s, 0);
+            const int64_t kbs = kb + (int64_t)kstep * s;
+            const uint32_t grp = (uint32_t)(kbs & 255) + ko;
+            const float sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                 ss, (grp >> 8) << 2, (int)((kbs >> 8) << 2), 0));
+            return RawConst{qv, sv};
+        } else {
+            return RawConst{0, __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ks, ko << 2, 4 * kstep * s, 0))};
+        }
+    };
+
+    auto xbuf = [&](int b) { return (uint16_t*)(s_mem + kLutBytes + b * kBXBuf); };
+    uint16_t* wreg = (uint16_t*)(s_mem + kLutBytes + 2 * kBXBuf + wv * kBWReg);
+    const int xw = (t >> 3) * 64 + 8 * ((t & 7) ^ ((t >> 3) & 7));   // staging slot of row t >> 3
+    int xrd[4];   // x fragment reads: row 32 i + q, chunk 2 kk + h
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) xrd[kk] = q * 64 + 8 * ((2 * kk + h) ^ (q & 7));
+    int wrd[2][4][2];   // transposing reads [j][kk][t]: row 16 kk + 8 h + 4 t + (l % 16) / 4,
+                        // columns 32 j + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 16 * kk + 8 * h + 4 * u + ((lane & 15) >> 2);
+                const int col = 32 * j + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                wrd[j][kk][u] = r * 64 + 8 * wslot(r, col >> 3) + (col & 7);
+            }
+
+    u32x4 xr[MT];
+    auto st_x = [&](uint16_t* X) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) *(u32x4*)(X + xw + 32 * i * 64) = xr[i];
+    };
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, 0);
+    st_x(xbuf(0));
+    if (!live) {
+        // idle columns: stage x as the live waves do, barrier for barrier
+        __syncthreads();
+        for (int s = 0; s < nsteps; ++s) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, s + 1 < nsteps ? s + 1 : s);
+            st_x(xbuf((s + 1) & 1));
+            __syncthreads();
+        }
+        return;
+    }
+
+    // dequantisation of one row block: 32 code bytes (two 16-byte halves) with
+    // constant a, as 8 chunks of eight 16-bit values, written to the region
+    u32x4 cw_[2], cq_[2], y[8];
+    RawConst kw, kq;
+    f2 lv[2][8];   // level pairs of eight code bytes, two groups in flight
+    auto lut_rd = [&](int grp, f2 (&d)[8]) {   // code bytes 8 grp .. 8 grp + 7
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint32_t c = cw_[grp >> 1][2 * (grp & 1) + (b >> 2)];
+            d[b] = *(const f2*)(lut + __builtin_amdgcn_perm(c, lb, 0x02020000u | ((4u + (b & 3)) << 8)));
+        }
+    };
+    auto mulcvt = [&](int grp, const f2 (&p)[8], float a) {   // chunks 2 grp, 2 grp + 1
+#pragma unroll
+        for (int b = 0; b < 8; ++b) y[2 * grp + (b >> 2)][b & 3] = pack16<DT>(p[b].x * a, p[b].y * a);
+    };
+    auto st_w = [&]() {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) *(u32x4*)(wreg + lane * 64 + 8 * wslot(lane, c)) = y[c];
+    };
+    // first step's W piece, synchronously
+    cw_[0] = ld_c(0, 0); cw_[1] = ld_c(1, 0); kw = ld_k(0);
+    {
+        const float a = block_const<DQ>(kw);
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) { lut_rd(grp, lv[0]); mulcvt(grp, lv[0], a); }
+        st_w();
+    }
+    // codes of step 1 (dequantised during step 0)
+    const int s1 = nsteps > 1 ? 1 : 0;
+    cw_[0] = ld_c(0, s1); cw_[1] = ld_c(1, s1); kw = ld_k(s1);
+    __syncthreads();   // level table and the first x tile
+
+    f32x16 acc[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    typedef typename Frag8<DT>::T F;
+    F fa[2][MT], fb[2][4];
+    auto rd_x = [&](const uint16_t* X, int kk, F (&d)[MT]) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) d[i] = *(const F*)(X + xrd[kk] + 32 * i * 64);
+    };
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    auto rd_w = [&]() {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(wreg + wrd[j][kk][0])));
+                const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(wreg + wrd[j][kk][1])));
+                fb[j][kk] = __builtin_bit_cast(F, u32x4{lo.x, lo.y, hi.x, hi.y});
+            }
+    };
+    auto mm = [&](int kk, const F (&a)[MT]) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            acc[i][0] = mfma32<DT>(a[i], fb[0][kk], acc[i][0]);
+            acc[i][1] = mfma32<DT>(a[i], fb[1][kk], acc[i][1]);
+        }
+    };
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, MT == 8 ? 1 : 2, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, MT == 8 ? 2 : 4, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int s = 0; s < nsteps; ++s) {
+        // loads: x rows of step s + 1, codes and constant of step s + 2 (past
+        // the end the last step again: in bounds, unused)
+        const int sx = s + 1 < nsteps ? s + 1 : s;
+        const int sc = s + 2 < nsteps ? s + 2 : nsteps - 1;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) xr[i] = ld_x(i, sx);
+        cq_[0] = ld_c(0, sc); cq_[1] = ld_c(1, sc); kq = ld_k(sc);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint16_t* X = xbuf(s & 1);
+        rd_w();              // this step's weight fragments (region written last step)
+        rd_x(X, 0, fa[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        const float a = block_const<DQ>(kw);
+        mm(0, fa[0]); rd_x(X, 1, fa[1]); lut_rd(0, lv[0]);
+        interleave();
+        mm(1, fa[1]); rd_x(X, 2, fa[0]); lut_rd(1, lv[1]); mulcvt(0, lv[0], a);
+        interleave();
+        mm(2, fa[0]); rd_x(X, 3, fa[1]); lut_rd(2, lv[0]); mulcvt(1, lv[1], a);
+        interleave();
+        mm(3, fa[1]); lut_rd(3, lv[1]); mulcvt(2, lv[0], a);
+        interleave();
+        mulcvt(3, lv[1], a);
+        st_w();              // next step's piece: after this step's transposing reads (in order)
+        st_x(xbuf((s + 1) & 1));
+        cw_[0] = cq_[0]; cw_[1] = cq_[1]; kw = kq;
+        __syncthreads();
+    }
+
+    const bool full = m0 + 32 * MT <= g.M;
+    const int64_t rbase = m0 + 4 * h;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = rbase + 32 * i + 8 * (r >> 2) + (r & 3);
+                const int64_t col = cw + 32 * j + q;
+                if (full || row < g.M) {
+                    if constexpr (PART)
+                        ((GLOBAL float*)g.part)[(int64_t)split * g.M * g.ldo + row * g.ldo + col] = acc[i][j][r];
+                    else if constexpr (OUT_F32)
+                        ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
+                    else
+                        ((GLOBAL uint16_t*)g.out)[row * g.ldo + col] = (uint16_t)pack16<DT>(acc[i][j][r], 0.0f);
+                }
+            }
+}
+
+template <int DT, bool DQ, bool OUT_F32, bool PART>
+__global__ __launch_bounds__(256, 1) void k_nf4_mm_bwd(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_mem[kBLds];
+    const int t = threadIdx.x;
+    {
+        const uint32_t lo = __builtin_bit_cast(uint32_t, level_imm(t & 15));
+        const uint32_t hi = __builtin_bit_cast(uint32_t, level_imm(t >> 4));
+        u32x4* row = (u32x4*)(s_mem + 256 * t);
+#pragma unroll
+        for (int c = 0; c < kLutCopies / 2; ++c) row[(c + t) & (kLutCopies / 2 - 1)] = u32x4{lo, hi, lo, hi};
+    }
+    int64_t tile;
+    int half = -1;
+    if (g.nhalf == 0) {
+        tile = g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
+    } else {
+        const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3, hpx = g.nhalf >> 2;
+        if (i < fpx) {
+            tile = x * fpx + i;
+        } else {
+            const int64_t hh = x * hpx + (i - fpx);
+            tile = g.nfull + (hh >> 1);
+            half = (int)(hh & 1);
+        }
+    }
+    const int split = PART ? (int)(tile / g.ntiles) : 0;
+    if (PART) tile -= (int64_t)split * g.ntiles;
+    int64_t mt, nt;
+    group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
+    if (half < 0) mm_bwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
+    else mm_bwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * half, nt * kXN, split);
 }
 
 // ---- few tokens, forward: one wave per 16 W rows and one part of the reduction
@@ -920,9 +1195,36 @@ hipError_t mm_fwd_go(GemmArgs g, hipStream_t s)
     return hipSuccess;
 }
 
+template <int DT, bool DQ, bool OUT_F32>
+hipError_t mm_bwd_go(GemmArgs g, hipStream_t s)
+{
+    g.ntn = (g.ncol + kXN - 1) / kXN;
+    g.ntiles = ((g.M + kXM - 1) / kXM) * g.ntn;
+    g.nfull = g.ntiles;
+    g.nhalf = 0;
+    g.tile0 = 0;
+    const int64_t ncu = cu_count(), total = g.ntiles;
+    if (ncu > 0 && total > ncu) {
+        const int64_t rem = total % ncu, full = total - rem;
+        if (rem > 0 && 2 * rem <= ncu && full % 8 == 0 && rem % 4 == 0) {
+            g.nfull = full;
+            g.nhalf = rem;
+        }
+    }
+    const int64_t blocks = g.nfull + 2 * g.nhalf;
+    if (blocks > kMaxGemmGrid) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_nf4_mm_bwd<DT, DQ, OUT_F32, false>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
 template <int DT, bool FWD, bool DQ, bool OUT_F32>
 hipError_t gemm_go(GemmArgs g, hipStream_t s)
 {
+    if constexpr (!FWD) {
+        // 32-bit buffer offsets: 256 rows of x under 2 GiB, codes under 2 GiB
+        if (g.nsplit <= 1 && g.M > 128 && g.kred < (int64_t(1) << 22) && g.kred * g.ncol < (int64_t(1) << 32))
+            return mm_bwd_go<DT, DQ, OUT_F32>(g, s);
+    }
     if constexpr (FWD) {
         // 32-bit lane offsets: 256 rows of x (and of codes) under 2 GiB
         if (g.nsplit <= 1 && g.M > 128 && g.kred < (int64_t(1) << 22)) return mm_fwd_go<DT, DQ, OUT_F32>(g, s);
