@@ -393,9 +393,15 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
         "library_bf16_bwd_ms": round(t_lib_b, 4), "library_bf16_bwd_TFLOPs": tf(t_lib_b),
         "dequant_ms_scaled": round(t_deq, 4),
         "dequant_then_library_fwd_ms": round(t_deq + t_lib_f, 4),
+        "dequant_then_library_bwd_ms": round(t_deq + t_lib_b, 4),
+        "fused_over_dequant_library_fwd": round(t_fwd / (t_deq + t_lib_f), 4),
+        "fused_over_dequant_library_bwd": round(t_bwd / (t_deq + t_lib_b), 4),
         "roofline": {"bound": "mfma", "kernel": "nf4_matmul forward",
                      "achieved": tf(t_fwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tf(t_fwd) / MFMA_BF16_PEAK_TFS, 4)},
+        "roofline_bwd": {"bound": "mfma", "kernel": "nf4_matmul backward",
+                         "achieved": tf(t_bwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tf(t_bwd) / MFMA_BF16_PEAK_TFS, 4)},
     }
     # few tokens (nf4_matmul_ws: the few-token forward kernel at m <= 32, else
     # the split reduction) against dequantise + library GEMM

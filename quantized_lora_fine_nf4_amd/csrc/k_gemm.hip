@@ -5,30 +5,40 @@
 // the forward and the backward pass ("QLoRA" paper summary page, How It
 // Works); AQLoRA names that per-step dequantisation as where quantised
 // fine-tuning loses its time (AQLoRA arXiv listing, English abstract).  Here
-// the weight tile is dequantised straight into LDS, in the value the codec
-// defines (y = RNE16(fl32(level[code] * dequantised absmax)), bitwise what
+// every weight is dequantised on chip, to the value the codec defines
+// (y = RNE16(fl32(level[code] * dequantised absmax)), bitwise what
 // nf4_dequantize writes), and multiplied there: the 16-bit weight never goes
 // to HBM.
 //
 //   forward   out[m, n] = sum_k x[m, k] * W[n, k]      (x: m x cols, out: m x rows)
 //   backward  out[m, k] = sum_n x[m, n] * W[n, k]      (x: m x rows, out: m x cols)
 //
-// One kernel serves both: the first operand A is always row-major with the
-// reduction index contiguous (x, or the output gradient); the W tile is
-// stored in LDS with the reduction index contiguous too -- in W's own order
-// forward, transposed backward -- so the MFMA fragment reads are the same.
+// Products of two bf16 (or fp16) values are exact in fp32; only the fp32
+// accumulation rounds.  Four kernels, chosen by m and direction:
+//   * m > 128: 256 x 256 output tiles, one workgroup of four waves per CU
+//     (k_nf4_mm_fwd: the weight fragments dequantised straight into MFMA
+//     registers; k_nf4_mm_bwd: each wave's weight piece transposed through LDS
+//     with the transposing read).  Tiles left over after the last whole round
+//     run as two 128-row halves.
+//   * m <= 128 (and any split reduction): k_nf4_matmul, 128 x 128 tiles, three
+//     workgroups per CU, the weight tile dequantised into LDS (transposed on
+//     the way backward).
+//   * forward with m <= 32 and a workspace: k_nf4_gemv16, one wave per 16
+//     weight rows on the 16 x 16 x 32 MFMA.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 output tile in k-steps
-// of 64 (one quantisation block of a W row forward); waves in a 2 x 2 grid,
-// each 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation.  The next step's A rows and W codes are loaded into registers
-// (raw: no wait) while the current step multiplies; after a barrier they are
-// dequantised into the single LDS buffer.  39 KB of LDS per workgroup lets 3
-// workgroups share a CU, which measured faster than double buffering at 2.
-// Level lookups read a 256-entry table of level pairs (one 8-byte read per
-// code byte).  Tiles are handed out in groups of 4 row tiles, each XCD taking
-// a contiguous run of that order.  Products of two bf16 values are exact in
-// fp32; only the fp32 accumulation rounds.
+// k_nf4_matmul: the first operand A is row-major with the reduction index
+// contiguous (x, or the output gradient); the W tile is stored in LDS with the
+// reduction index contiguous too -- in W's own order forward, transposed
+// backward -- so the MFMA fragment reads are the same.  A 256-thread
+// workgroup computes a 128 x 128 output tile in k-steps of 64 (one
+// quantisation block of a W row forward); waves in a 2 x 2 grid, each
+// 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  The next step's A rows
+// and W codes are loaded into registers (raw: no wait) while the current step
+// multiplies; after a barrier they are dequantised into the single LDS
+// buffer.  39 KB of LDS per workgroup lets 3 workgroups share a CU.  Level
+// lookups read a 256-entry table of level pairs (one 8-byte read per code
+// byte).  Tiles are handed out in groups of 4 row tiles, each XCD taking a
+// contiguous run of that order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,26 +51,8 @@
 namespace nf4k {
 namespace {
 
-#ifndef NF4_GEMM_STAGES
-#define NF4_GEMM_STAGES 1         // LDS buffers; one (two barriers per step) leaves room for 3 workgroups per CU
-#endif
-#ifndef NF4_GEMM_GROUP_M
-#define NF4_GEMM_GROUP_M 4        // output row tiles per group of the tile order (0: row-major order)
-#endif
-#ifndef NF4_GEMM_XCD
-#define NF4_GEMM_XCD 1            // give each XCD a contiguous run of the tile order
-#endif
-#ifndef NF4_GEMM_LUT2
-#define NF4_GEMM_LUT2 1           // copies of a 256-entry table of level pairs (0: 16-entry level table)
-#endif
-#ifndef NF4_GEMM_WM
-#define NF4_GEMM_WM 64            // output rows per wave
-#endif
-#ifndef NF4_GEMM_WN
-#define NF4_GEMM_WN 64            // output columns per wave
-#endif
 constexpr int kGThreads = 256;
-constexpr int kWM = NF4_GEMM_WM, kWN = NF4_GEMM_WN;
+constexpr int kWM = 64, kWN = 64;  // output rows and columns per wave
 constexpr int kTM = kWM / 32, kTN = kWN / 32;   // 32 x 32 MFMA tiles per wave
 constexpr int kBM = 2 * kWM;      // output rows (of x) per workgroup
 constexpr int kBN = 2 * kWN;      // output columns per workgroup
@@ -175,19 +167,13 @@ template <int DT>
 __device__ __forceinline__ u32x4 deq8(uint32_t c, float adq, const float* lv)
 {
     u32x4 r;
-#if NF4_GEMM_LUT2
-    // lv: 256 (level[b & 15], level[b >> 4]) pairs per copy, copy chosen by lane
-    const f2* lp = (const f2*)lv + 256 * ((threadIdx.x & 63) % NF4_GEMM_LUT2);
+    // lv: 256 (level[b & 15], level[b >> 4]) pairs
+    const f2* lp = (const f2*)lv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const f2 p = lp[(c >> (8 * j)) & 255];
         r[j] = pack16<DT>(p.x * adq, p.y * adq);
     }
-#else
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        r[j] = pack16<DT>(lv[(c >> (8 * j)) & 15] * adq, lv[(c >> (8 * j + 4)) & 15] * adq);
-#endif
     return r;
 }
 
@@ -275,52 +261,50 @@ __device__ __forceinline__ void store_step(const StepRegs& r, uint16_t* As, uint
     }
 }
 
-#ifndef NF4_GEMM_MIN_WG
-#define NF4_GEMM_MIN_WG 3         // workgroups per CU the register allocation must allow
-#endif
+
+// Tile t of a launch of n workgroups in an order where each XCD (workgroups
+// are dealt to the eight XCDs in turn) takes a contiguous run of tiles.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n)
+{
+    const int64_t per = n >> 3, rem = n & 7, x = b & 7, i = b >> 3;
+    return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}
+
+// Output tile coordinates in groups of four row tiles, column tiles outer.
+__device__ __forceinline__ void group_coords(int64_t tile, int64_t mtiles, int64_t ntn, int64_t& mt, int64_t& nt)
+{
+    constexpr int kG = 4;
+    const int64_t per = kG * ntn, first = (tile / per) * kG;
+    const int64_t gsz = mtiles - first < kG ? mtiles - first : kG;
+    const int64_t in = tile % per;
+    mt = first + in % gsz;
+    nt = in / gsz;
+}
 
 // PART: this workgroup sums one split of the reduction and stores it as an
 // fp32 partial (k_splitk_sum adds the splits in order); otherwise the whole
 // reduction, stored as fp32 or the 16-bit type.
 template <int DT, bool FWD, bool DQ, bool OUT_F32, bool PART>
-__global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmArgs g)
+__global__ __launch_bounds__(kGThreads, 3) void k_nf4_matmul(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[NF4_GEMM_STAGES][kBM * kLdp];
-    __shared__ __attribute__((aligned(16))) uint16_t s_w[NF4_GEMM_STAGES][kBN * kLdp];
+    // one LDS buffer (two barriers per step) leaves room for 3 workgroups per CU
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[kBM * kLdp];
+    __shared__ __attribute__((aligned(16))) uint16_t s_w[kBN * kLdp];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     // level tables from immediates: an indexed constant table would be a
     // memory load, waited for before the first tile's loads are issued
-#if NF4_GEMM_LUT2
-    __shared__ __attribute__((aligned(16))) float s_lv[2 * 256 * NF4_GEMM_LUT2];
-    for (int i = t; i < 256 * NF4_GEMM_LUT2; i += kGThreads) {
-        const int b = i & 255;
-        s_lv[2 * i] = level_imm(b & 15);
-        s_lv[2 * i + 1] = level_imm(b >> 4);
+    __shared__ __attribute__((aligned(16))) float s_lv[2 * 256];
+    for (int i = t; i < 256; i += kGThreads) {
+        s_lv[2 * i] = level_imm(i & 15);
+        s_lv[2 * i + 1] = level_imm(i >> 4);
     }
-#else
-    __shared__ float s_lv[16];
-    if (t < 16) s_lv[t] = level_imm(t);
-#endif
 
-    int64_t tile = g.tile0 + blockIdx.x;
-    if (NF4_GEMM_XCD && (gridDim.x & 7) == 0)
-        tile = g.tile0 + (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    int64_t tile = g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
     // splits are the outer index: each split covers every output tile
     const int split = PART ? (int)(tile / g.ntiles) : 0;
     if (PART) tile -= (int64_t)split * g.ntiles;
     int64_t mt, nt;
-    if (NF4_GEMM_GROUP_M > 0) {
-        const int64_t per = (int64_t)NF4_GEMM_GROUP_M * g.ntn;
-        const int64_t first = (tile / per) * NF4_GEMM_GROUP_M;
-        const int64_t mtiles = (g.M + kBM - 1) / kBM;
-        const int64_t gsz = mtiles - first < NF4_GEMM_GROUP_M ? mtiles - first : NF4_GEMM_GROUP_M;
-        const int64_t in = tile % per;
-        mt = first + in % gsz;
-        nt = in / gsz;
-    } else {
-        mt = tile / g.ntn;
-        nt = tile % g.ntn;
-    }
+    group_coords(tile, (g.M + kBM - 1) / kBM, g.ntn, mt, nt);
     const int64_t m0 = mt * kBM;
     const int64_t c0 = nt * kBN;
     const int wm = wv >> 1, wn = wv & 1;   // this wave's kWM x kWN quarter
@@ -340,15 +324,14 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
     StepRegs regs;
     load_step<FWD, DQ>(regs, g, m0, c0, kb);
     __syncthreads();   // level table
-    store_step<DT, FWD, DQ>(regs, s_a[0], s_w[0], s_lv);
+    store_step<DT, FWD, DQ>(regs, s_a, s_w, s_lv);
     __syncthreads();
 
     for (int s = 0; s < nsteps; ++s) {
-        const int cur = NF4_GEMM_STAGES == 2 ? (s & 1) : 0;
         const bool more = s + 1 < nsteps;
         if (more) load_step<FWD, DQ>(regs, g, m0, c0, kb + (int64_t)(s + 1) * kBK);
-        const uint16_t* As = s_a[cur];
-        const uint16_t* Ws = s_w[cur];
+        const uint16_t* As = s_a;
+        const uint16_t* Ws = s_w;
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int kof = 16 * kk + 8 * (lane >> 5);
@@ -366,9 +349,8 @@ __global__ __launch_bounds__(kGThreads, NF4_GEMM_MIN_WG) void k_nf4_matmul(GemmA
                 for (int j = 0; j < kTN; ++j)
                     acc[i][j] = mfma32<DT>(fa[i], fb[j], acc[i][j]);
         }
-        if (NF4_GEMM_STAGES == 1) __syncthreads();   // every wave done reading the one buffer
-        if (more) store_step<DT, FWD, DQ>(regs, s_a[cur ^ (NF4_GEMM_STAGES - 1)],
-                                      s_w[cur ^ (NF4_GEMM_STAGES - 1)], s_lv);
+        __syncthreads();   // every wave done reading the one buffer
+        if (more) store_step<DT, FWD, DQ>(regs, s_a, s_w, s_lv);
         __syncthreads();
     }
 
@@ -417,25 +399,6 @@ constexpr int kLutCopies = 32;
 constexpr int kLutBytes = 256 * kLutCopies * 8;
 constexpr int kXBuf = kXM * kXPitch * 2;      // bytes per x buffer
 constexpr int kXLds = kLutBytes + 2 * kXBuf;  // 139,264 B of LDS: one workgroup per CU
-
-// Tile t of a launch of n workgroups in an order where each XCD (workgroups
-// are dealt to the eight XCDs in turn) takes a contiguous run of tiles.
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n)
-{
-    const int64_t per = n >> 3, rem = n & 7, x = b & 7, i = b >> 3;
-    return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
-}
-
-// Output tile coordinates in groups of four row tiles, column tiles outer.
-__device__ __forceinline__ void group_coords(int64_t tile, int64_t mtiles, int64_t ntn, int64_t& mt, int64_t& nt)
-{
-    constexpr int kG = 4;
-    const int64_t per = kG * ntn, first = (tile / per) * kG;
-    const int64_t gsz = mtiles - first < kG ? mtiles - first : kG;
-    const int64_t in = tile % per;
-    mt = first + in % gsz;
-    nt = in / gsz;
-}
 
 // Eight codes (one dword, element 2j in the low nibble of byte j) to eight
 // 16-bit values through the level-pair table; lb = this lane's copy offset.
@@ -724,14 +687,17 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
 // as column C + i, rows r .. r + 3.  The step's dequantisation runs one step
 // ahead of its MFMAs, spread over the four sub-steps; x is double-buffered as
 // in the forward kernel.  Region rows are 128 B with chunk c of row r at slot
-// c ^ (2 (r % 4) + (r / 4) % 2), conflict-free for both the row writes and
-// the transposing reads; x rows are 128 B with chunk c of row r at c ^ (r % 8).
+// c ^ (4 ((r / 2) % 2) + (r / 4) % 4), conflict-free for both the row writes and
+// the transposing reads; x rows are 128 B with chunk c of row r at
+// c ^ ((r / 2) % 8).  (LDS serves 256 B per cycle: two consecutive 128-byte
+// rows fall in different bank halves, so the swizzles separate rows of equal
+// parity.)
 constexpr int kBXBuf = 256 * 128;                   // x buffer: 256 rows x 64 16-bit values
 constexpr int kBWReg = 64 * 128;                    // per-wave W region: 64 rows x 64 16-bit values
 constexpr int kBLds = kLutBytes + 2 * kBXBuf + 4 * kBWReg;   // 163,840 B
 static_assert(kBLds <= 163840, "LDS of one CU");
 
-__device__ __forceinline__ int wslot(int r, int c) { return c ^ (((r & 3) << 1) | ((r >> 2) & 1)); }
+__device__ __forceinline__ int wslot(int r, int c) { return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)); }
 
 template <int DT, bool DQ, bool OUT_F32, bool PART, int MT>
 __device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split)
@@ -787,10 +753,10 @@ __device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, i
 
     auto xbuf = [&](int b) { return (uint16_t*)(s_mem + kLutBytes + b * kBXBuf); };
     uint16_t* wreg = (uint16_t*)(s_mem + kLutBytes + 2 * kBXBuf + wv * kBWReg);
-    const int xw = (t >> 3) * 64 + 8 * ((t & 7) ^ ((t >> 3) & 7));   // staging slot of row t >> 3
+    const int xw = (t >> 3) * 64 + 8 * ((t & 7) ^ ((t >> 4) & 7));   // staging slot of row t >> 3
     int xrd[4];   // x fragment reads: row 32 i + q, chunk 2 kk + h
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) xrd[kk] = q * 64 + 8 * ((2 * kk + h) ^ (q & 7));
+    for (int kk = 0; kk < 4; ++kk) xrd[kk] = q * 64 + 8 * ((2 * kk + h) ^ ((q >> 1) & 7));
     int wrd[2][4][2];   // transposing reads [j][kk][t]: row 16 kk + 8 h + 4 t + (l % 16) / 4,
                         // columns 32 j + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3
 #pragma unroll

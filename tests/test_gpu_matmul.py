@@ -6,8 +6,8 @@ fp64 product.  Bound (fp32 accumulation of exact bf16 or fp16 products over K
 terms): |out - ref| <= 2 K 2^-24 (|x| |W|^T) elementwise.  The 16-bit output
 equals the round-to-nearest-even of the same kernel's fp32 output.  bf16 and
 fp16, ragged m (1, 77, 300), several tile counts, double quant on and off,
-forward and backward; the 14B stack's FFN shape (13824 x 5120) at m = 4096
-on sampled rows.  The split-reduction path (nf4_matmul_ws) on shapes it
+forward and backward; a shape whose last tiles run as halves, every element;
+the 14B stack's FFN shape (13824 x 5120) at m = 4096 on sampled rows.  The split-reduction path (nf4_matmul_ws) on shapes it
 splits, against the same bound, deterministic, and the FFN shape at m = 16
 and 32; its few-token forward kernel (m <= 32: 1, 5, 16, 17, 32) the same way.
 """
@@ -132,6 +132,22 @@ def test_matmul_fullsize_ffn_sampled(backward, dtype):
     idx = np.sort(np.r_[0, m - 1, rng.integers(0, m, 6)])
     worst = _check(out, xb, W, backward, rows_idx=idx)
     print(f"[{'bwd' if backward else 'fwd'}] worst error / bound {worst:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_matmul_tail_halves_match_oracle(backward):
+    """260 output tiles of 256 x 256 on 256 CUs: the 4 tiles past the whole
+    round run as 128-row halves, one of them over the ragged last 228 rows;
+    every output element is checked."""
+    m = 3300
+    rows, cols = (256, 5120) if backward else (5120, 256)
+    print_case("nf4_matmul tail halves", m, rows, cols, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 515, True, outliers=0.001)
+    xb = _x(m, rows if backward else cols, 516)
+    out = _run(W, xb, backward)
+    _check(out, xb, W, backward)
+    o16 = _run(W, xb, backward, out_f32=False)
+    assert torch.equal(o16, out.to(torch.bfloat16))
 
 
 def _run_ws(W, xb, backward, out_f32=True):
