@@ -185,8 +185,10 @@ def test_split_reduction_matches_oracle(m, dtype, backward):
     assert torch.equal(o16, out.to(TORCH16[dtype]))
 
 
-# parts of 1 super-chunk (3 and 8 parts), and 2 super-chunks with a last part of 1 (6 parts)
-@pytest.mark.parametrize("shape", [(256, 384), (128, 1024), (8192, 1408)], ids=lambda s: f"{s[0]}x{s[1]}")
+# parts of 1 super-chunk (3 and 8 parts), 2 super-chunks with a last part of 1
+# (6 parts), and 2 super-chunks in 10 parts over 68 workgroups of 64 rows
+@pytest.mark.parametrize("shape", [(256, 384), (128, 1024), (8192, 1408), (4352, 2560)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
 @pytest.mark.parametrize("dq", [False, True], ids=["nodq", "dq"])
 @pytest.mark.parametrize("dtype", [BF16, FP16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 32])
