@@ -19,7 +19,8 @@
 //     (k_nf4_mm_fwd: the weight fragments dequantised straight into MFMA
 //     registers; k_nf4_mm_bwd: each wave's weight piece transposed through LDS
 //     with the transposing read).  Tiles left over after the last whole round
-//     run as two 128-row halves.
+//     run as 128-row halves (or, backward, 64-row quarters when those fit one
+//     round).
 //   * m <= 128 (and any split reduction): k_nf4_matmul, 128 x 128 tiles, three
 //     workgroups per CU, the weight tile dequantised into LDS (transposed on
 //     the way backward).
@@ -124,7 +125,8 @@ struct GemmArgs {
     int64_t tile0;          // first (tile, split) index of this launch
     int64_t ntiles;         // output tiles (row tiles x column tiles)
     int nsplit;             // splits of the reduction (1: none)
-    int64_t nfull, nhalf;   // 256 x 256 forward tiles: whole tiles, then tiles split in two halves (0: none)
+    int64_t nfull, nhalf;   // 256 x 256 tiles: whole tiles, then nhalf tiles split into row pieces (0: none)
+    int pieces;             // row pieces of each of those tiles: 2 (128 rows) or 4 (64 rows, backward)
     int split_steps;        // k-steps per split
     float* part;            // nsplit > 1: fp32 partials [nsplit][M x ncol]
 };
@@ -860,8 +862,8 @@ __device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, i
 #pragma unroll
         for (int i = 0; i < 2 * MT; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, MT == 8 ? 1 : 2, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, MT == 8 ? 2 : 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 / MT, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 16 / MT, 0);  // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -927,26 +929,34 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_bwd(GemmArgs g)
 #pragma unroll
         for (int c = 0; c < kLutCopies / 2; ++c) row[(c + t) & (kLutCopies / 2 - 1)] = u32x4{lo, hi, lo, hi};
     }
+    // With nhalf > 0: nfull whole tiles, then nhalf tiles cut into g.pieces row
+    // pieces (the tiles left over after the whole rounds of one workgroup per
+    // CU); every XCD takes its share of whole tiles and then of pieces, both
+    // contiguous in the tile order.  Each wave dequantises its weight piece
+    // whatever the rows, so a 64-row quarter costs more than a quarter of a
+    // tile, but the pieces of the last tiles fill one short round.
     int64_t tile;
-    int half = -1;
+    int piece = -1;
     if (g.nhalf == 0) {
         tile = g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
     } else {
-        const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3, hpx = g.nhalf >> 2;
+        const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3;
+        const int64_t ppx = g.nhalf * g.pieces >> 3;
         if (i < fpx) {
             tile = x * fpx + i;
         } else {
-            const int64_t hh = x * hpx + (i - fpx);
-            tile = g.nfull + (hh >> 1);
-            half = (int)(hh & 1);
+            const int64_t pp = x * ppx + (i - fpx);
+            tile = g.nfull + pp / g.pieces;
+            piece = (int)(pp % g.pieces);
         }
     }
     const int split = PART ? (int)(tile / g.ntiles) : 0;
     if (PART) tile -= (int64_t)split * g.ntiles;
     int64_t mt, nt;
     group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
-    if (half < 0) mm_bwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
-    else mm_bwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * half, nt * kXN, split);
+    if (piece < 0) mm_bwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
+    else if (g.pieces == 2) mm_bwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * piece, nt * kXN, split);
+    else mm_bwd_tile<DT, DQ, OUT_F32, PART, 2>(g, s_mem, mt * kXM + 64 * piece, nt * kXN, split);
 }
 
 // ---- few tokens, forward: one wave per 16 W rows and one part of the reduction
@@ -1169,15 +1179,23 @@ hipError_t mm_bwd_go(GemmArgs g, hipStream_t s)
     g.nfull = g.ntiles;
     g.nhalf = 0;
     g.tile0 = 0;
+    g.pieces = 2;
     const int64_t ncu = cu_count(), total = g.ntiles;
     if (ncu > 0 && total > ncu) {
         const int64_t rem = total % ncu, full = total - rem;
-        if (rem > 0 && 2 * rem <= ncu && full % 8 == 0 && rem % 4 == 0) {
-            g.nfull = full;
-            g.nhalf = rem;
+        if (rem > 0 && full % 8 == 0) {
+            // quarters when they fit one round, else halves
+            if (4 * rem <= ncu && rem % 2 == 0) {
+                g.nfull = full;
+                g.nhalf = rem;
+                g.pieces = 4;
+            } else if (2 * rem <= ncu && rem % 4 == 0) {
+                g.nfull = full;
+                g.nhalf = rem;
+            }
         }
     }
-    const int64_t blocks = g.nfull + 2 * g.nhalf;
+    const int64_t blocks = g.nfull + g.pieces * g.nhalf;
     if (blocks > kMaxGemmGrid) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_nf4_mm_bwd<DT, DQ, OUT_F32, false>), dim3((unsigned)blocks), dim3(256), 0, s, g);
     return hipGetLastError();
@@ -1336,6 +1354,7 @@ hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabs
     g.ntiles = ((m + kBM - 1) / kBM) * g.ntn;
     g.nfull = g.ntiles;
     g.nhalf = 0;
+    g.pieces = 2;
     const int ksteps = (int)(g.kred / kBK);
     g.nsplit = (part && nsplit > 1) ? nsplit : 1;
     g.split_steps = (ksteps + g.nsplit - 1) / g.nsplit;

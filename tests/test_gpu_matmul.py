@@ -134,12 +134,14 @@ def test_matmul_fullsize_ffn_sampled(backward, dtype):
     print(f"[{'bwd' if backward else 'fwd'}] worst error / bound {worst:.3f}", flush=True)
 
 
+@pytest.mark.parametrize("m", [3300, 3100])
 @pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
-def test_matmul_tail_halves_match_oracle(backward):
+def test_matmul_tail_halves_match_oracle(backward, m):
     """260 output tiles of 256 x 256 on 256 CUs: the 4 tiles past the whole
-    round run as 128-row halves, one of them over the ragged last 228 rows;
-    every output element is checked."""
-    m = 3300
+    round run in row pieces (128-row halves forward, 64-row quarters
+    backward), some of them over the ragged last 228 or 28 rows and, at
+    m = 3100, some entirely past the last row; every output element is
+    checked."""
     rows, cols = (256, 5120) if backward else (5120, 256)
     print_case("nf4_matmul tail halves", m, rows, cols, "bwd" if backward else "fwd")
     W = DevWeight(rows, cols, 515, True, outliers=0.001)
