@@ -19,8 +19,7 @@
 //     (k_nf4_mm_fwd: the weight fragments dequantised straight into MFMA
 //     registers; k_nf4_mm_bwd: each wave's weight piece transposed through LDS
 //     with the transposing read).  Tiles left over after the last whole round
-//     run as 128-row halves (or, backward, 64-row quarters when those fit one
-//     round).
+//     run as 64-row quarters, or 128-row halves, when those fit one round.
 //   * m <= 128 (and any split reduction): k_nf4_matmul, 128 x 128 tiles, three
 //     workgroups per CU, the weight tile dequantised into LDS (transposed on
 //     the way backward).
@@ -562,8 +561,8 @@ __device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, i
 #pragma unroll
         for (int i = 0; i < 2 * MT; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, MT == 8 ? 1 : 2, 0);   // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, MT == 8 ? 2 : 4, 0);   // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 / MT, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 16 / MT, 0);  // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -632,11 +631,24 @@ __device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, i
 }
 
 
-// The launch order: with nhalf > 0 it holds nfull whole tiles, then nhalf
-// tiles each split in two halves of 128 x rows (the tiles left over after the
-// whole rounds of one workgroup per CU: splitting them shortens the last
-// round); every XCD takes its share of whole tiles first and then its share of
-// halves, both contiguous in the tile order.
+// The launch order of both large-m kernels: with nhalf > 0 it holds nfull
+// whole tiles, then nhalf tiles cut into g.pieces row pieces of 128 or 64 rows
+// (the tiles left over after the whole rounds of one workgroup per CU: cutting
+// them shortens the last round); every XCD takes its share of whole tiles
+// first and then its share of pieces, both contiguous in the tile order.
+// piece = -1 for a whole tile.
+__device__ __forceinline__ int64_t launch_tile(const GemmArgs& g, int& piece)
+{
+    piece = -1;
+    if (g.nhalf == 0) return g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3;
+    const int64_t ppx = g.nhalf * g.pieces >> 3;
+    if (i < fpx) return x * fpx + i;
+    const int64_t pp = x * ppx + (i - fpx);
+    piece = (int)(pp % g.pieces);
+    return g.nfull + pp / g.pieces;
+}
+
 template <int DT, bool DQ, bool OUT_F32, bool PART>
 __global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
 {
@@ -651,26 +663,15 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
 #pragma unroll
         for (int c = 0; c < kLutCopies / 2; ++c) row[(c + t) & (kLutCopies / 2 - 1)] = u32x4{lo, hi, lo, hi};
     }
-    int64_t tile;
-    int half = -1;
-    if (g.nhalf == 0) {
-        tile = g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
-    } else {
-        const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3, hpx = g.nhalf >> 2;
-        if (i < fpx) {
-            tile = x * fpx + i;
-        } else {
-            const int64_t hh = x * hpx + (i - fpx);
-            tile = g.nfull + (hh >> 1);
-            half = (int)(hh & 1);
-        }
-    }
+    int piece;
+    int64_t tile = launch_tile(g, piece);
     const int split = PART ? (int)(tile / g.ntiles) : 0;
     if (PART) tile -= (int64_t)split * g.ntiles;
     int64_t mt, nt;
     group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
-    if (half < 0) mm_fwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
-    else mm_fwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * half, nt * kXN, split);
+    if (piece < 0) mm_fwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
+    else if (g.pieces == 2) mm_fwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * piece, nt * kXN, split);
+    else mm_fwd_tile<DT, DQ, OUT_F32, PART, 2>(g, s_mem, mt * kXM + 64 * piece, nt * kXN, split);
 }
 
 // ---- large m, backward (input gradient): 256 x 256 output tiles, the weight
@@ -929,27 +930,11 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_bwd(GemmArgs g)
 #pragma unroll
         for (int c = 0; c < kLutCopies / 2; ++c) row[(c + t) & (kLutCopies / 2 - 1)] = u32x4{lo, hi, lo, hi};
     }
-    // With nhalf > 0: nfull whole tiles, then nhalf tiles cut into g.pieces row
-    // pieces (the tiles left over after the whole rounds of one workgroup per
-    // CU); every XCD takes its share of whole tiles and then of pieces, both
-    // contiguous in the tile order.  Each wave dequantises its weight piece
-    // whatever the rows, so a 64-row quarter costs more than a quarter of a
-    // tile, but the pieces of the last tiles fill one short round.
-    int64_t tile;
-    int piece = -1;
-    if (g.nhalf == 0) {
-        tile = g.tile0 + xcd_tile(blockIdx.x, gridDim.x);
-    } else {
-        const int64_t x = blockIdx.x & 7, i = blockIdx.x >> 3, fpx = g.nfull >> 3;
-        const int64_t ppx = g.nhalf * g.pieces >> 3;
-        if (i < fpx) {
-            tile = x * fpx + i;
-        } else {
-            const int64_t pp = x * ppx + (i - fpx);
-            tile = g.nfull + pp / g.pieces;
-            piece = (int)(pp % g.pieces);
-        }
-    }
+    // Each wave dequantises its weight piece whatever the rows, so a 64-row
+    // quarter costs more than a quarter of a tile, but the pieces of the last
+    // tiles fill one short round.
+    int piece;
+    int64_t tile = launch_tile(g, piece);
     const int split = PART ? (int)(tile / g.ntiles) : 0;
     if (PART) tile -= (int64_t)split * g.ntiles;
     int64_t mt, nt;
@@ -1128,27 +1113,42 @@ int cu_count()
     return n;
 }
 
+// Row pieces for the tiles left over after the last whole round of one
+// workgroup per CU (full whole tiles, rem left over): 64-row quarters when
+// four per tile fit one round, else 128-row halves when two do, each split
+// evenly across the 8 XCDs; 0 when neither applies.
+int tail_pieces(int64_t total, int64_t ncu, int64_t& full, int64_t& rem)
+{
+    if (ncu <= 0 || total <= ncu) return 0;
+    rem = total % ncu;
+    full = total - rem;
+    if (rem == 0 || full % 8 != 0) return 0;
+    if (4 * rem <= ncu && rem % 2 == 0) return 4;
+    if (2 * rem <= ncu && rem % 4 == 0) return 2;
+    return 0;
+}
+
 template <int DT, bool DQ, bool OUT_F32>
 hipError_t mm_fwd_go(GemmArgs g, hipStream_t s)
 {
     g.ntn = (g.ncol + kXN - 1) / kXN;
     g.ntiles = ((g.M + kXM - 1) / kXM) * g.ntn;
     const int64_t total = g.ntiles * g.nsplit;
-    // With one workgroup per CU, the tiles past the last whole round run as
-    // halves when those fit one round and the split is even across XCDs.
+    // With one workgroup per CU, the tiles past the last whole round run in
+    // row pieces when those fit one round.
     g.nfull = total;
     g.nhalf = 0;
-    const int64_t ncu = cu_count();
-    if (g.nsplit == 1 && ncu > 0 && total > ncu && total + ncu < kMaxGemmGrid) {
-        const int64_t rem = total % ncu, full = total - rem;
-        if (rem > 0 && 2 * rem <= ncu && full % 8 == 0 && rem % 4 == 0) {
-            g.nfull = full;
-            g.nhalf = rem;
-            g.tile0 = 0;
-            hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, false>), dim3((unsigned)(full + 2 * rem)), dim3(256),
-                               0, s, g);
-            return hipGetLastError();
-        }
+    g.pieces = 2;
+    int64_t full = 0, rem = 0;
+    const int pieces = g.nsplit == 1 ? tail_pieces(total, cu_count(), full, rem) : 0;
+    if (pieces > 0 && full + pieces * rem < kMaxGemmGrid) {
+        g.nfull = full;
+        g.nhalf = rem;
+        g.pieces = pieces;
+        g.tile0 = 0;
+        hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, false>), dim3((unsigned)(full + pieces * rem)), dim3(256),
+                           0, s, g);
+        return hipGetLastError();
     }
     for (int64_t t0 = 0; t0 < total; t0 += kMaxGemmGrid) {
         const int64_t n = total - t0 < kMaxGemmGrid ? total - t0 : kMaxGemmGrid;
@@ -1180,20 +1180,12 @@ hipError_t mm_bwd_go(GemmArgs g, hipStream_t s)
     g.nhalf = 0;
     g.tile0 = 0;
     g.pieces = 2;
-    const int64_t ncu = cu_count(), total = g.ntiles;
-    if (ncu > 0 && total > ncu) {
-        const int64_t rem = total % ncu, full = total - rem;
-        if (rem > 0 && full % 8 == 0) {
-            // quarters when they fit one round, else halves
-            if (4 * rem <= ncu && rem % 2 == 0) {
-                g.nfull = full;
-                g.nhalf = rem;
-                g.pieces = 4;
-            } else if (2 * rem <= ncu && rem % 4 == 0) {
-                g.nfull = full;
-                g.nhalf = rem;
-            }
-        }
+    int64_t full = 0, rem = 0;
+    const int pieces = tail_pieces(g.ntiles, cu_count(), full, rem);
+    if (pieces > 0) {
+        g.nfull = full;
+        g.nhalf = rem;
+        g.pieces = pieces;
     }
     const int64_t blocks = g.nfull + g.pieces * g.nhalf;
     if (blocks > kMaxGemmGrid) return hipErrorInvalidValue;
