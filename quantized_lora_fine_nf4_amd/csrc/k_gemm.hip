@@ -1113,6 +1113,60 @@ int cu_count()
     return n;
 }
 
+// Which kernel takes a call.  The choices are functions of the shape only
+// (the workspace a caller allocates depends on them), planned for the 256
+// CUs of an MI355X.
+constexpr int64_t kPlanCus = 256;
+
+// The 256 x 256 kernels keep 256 rows of x (and of the codes, backward the
+// whole weight) under 32-bit buffer offsets.
+bool big_eligible(bool forward, int64_t M, int64_t ncol, int64_t kred)
+{
+    if (M <= 128 || kred >= (int64_t(1) << 22)) return false;
+    return forward || kred * ncol < (int64_t(1) << 32);
+}
+
+// Without a split, the 256 x 256 kernels take a call when their tiles fill at
+// least half a round (forward) or when the 128 x 128 tiles would need more
+// than one (backward); below that the 128 x 128 kernel's more, shorter
+// workgroups finish first.  Measured on the 13824 x 5120 weight: forward
+// m = 512 (108 tiles) 0.117 ms on 128 x 128 tiles against 0.144, m = 768
+// (162) 0.145 against 0.160; backward m = 768 0.336 against 0.392, m = 1024
+// 0.393 against 0.483.
+bool use_big(bool forward, int64_t M, int64_t ncol, int64_t kred)
+{
+    if (!big_eligible(forward, M, ncol, kred)) return false;
+    if (forward) return ((M + kXM - 1) / kXM) * ((ncol + kXN - 1) / kXN) >= kPlanCus / 2;
+    return ((M + kBM - 1) / kBM) * (ncol / kBN) > kPlanCus;
+}
+
+// With a workspace, when the 256 x 256 tiles do not fill a round, their
+// reduction (80 k-steps forward and 216 backward on the FFN weight) is split
+// across workgroups (fp32 partials added in split order).  The split count
+// minimises rounds x k-steps per split plus the partials' traffic (about 0.05
+// k-step per (tile, split) workgroup: 512 KB written and read back at ~5 TB/s
+// against ~2 us per k-step), at least 16 k-steps per split and at most 16
+// splits, and is taken when it saves at least 15%.  0: no split.
+int big_splits(bool forward, int64_t M, int64_t ncol, int64_t kred)
+{
+    if (!big_eligible(forward, M, ncol, kred)) return 0;
+    const int64_t tiles = ((M + kXM - 1) / kXM) * ((ncol + kXN - 1) / kXN), ksteps = kred / 64;
+    if (tiles >= kPlanCus) return 0;
+    int64_t best = 1;
+    double best_cost = 0.85 * (double)ksteps;   // one round, unsplit, less the margin a split must win by
+    for (int64_t sp = 2; sp <= 16 && sp <= ksteps / 16; ++sp) {
+        const int64_t rounds = (tiles * sp + kPlanCus - 1) / kPlanCus, per = (ksteps + sp - 1) / sp;
+        const double cost = (double)(rounds * per) + 0.05 * (double)(tiles * sp);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = sp;
+        }
+    }
+    if (best < 2) return 0;
+    const int64_t per = (ksteps + best - 1) / best;
+    return (int)((ksteps + per - 1) / per);
+}
+
 // Row pieces for the tiles left over after the last whole round of one
 // workgroup per CU (full whole tiles, rem left over): 64-row quarters when
 // four per tile fit one round, else 128-row halves when two do, each split
@@ -1180,6 +1234,24 @@ hipError_t mm_bwd_go(GemmArgs g, hipStream_t s)
     g.nhalf = 0;
     g.tile0 = 0;
     g.pieces = 2;
+    if (g.nsplit > 1) {
+        // (tile, split) workgroups, each summing split_steps k-steps into an
+        // fp32 partial tile; k_splitk_sum adds the splits in order
+        const int64_t total = g.ntiles * g.nsplit;
+        for (int64_t t0 = 0; t0 < total; t0 += kMaxGemmGrid) {
+            const int64_t n = total - t0 < kMaxGemmGrid ? total - t0 : kMaxGemmGrid;
+            g.tile0 = t0;
+            hipLaunchKernelGGL((k_nf4_mm_bwd<DT, DQ, OUT_F32, true>), dim3((unsigned)n), dim3(256), 0, s, g);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int64_t n = g.M * g.ncol;
+        const int64_t blocks = (n / 4 + 255) / 256;
+        if (blocks > kMaxGemmGrid) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_splitk_sum<DT, OUT_F32>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           (const float*)g.part, g.nsplit, n, g.out);
+        return hipGetLastError();
+    }
     int64_t full = 0, rem = 0;
     const int pieces = tail_pieces(g.ntiles, cu_count(), full, rem);
     if (pieces > 0) {
@@ -1196,14 +1268,12 @@ hipError_t mm_bwd_go(GemmArgs g, hipStream_t s)
 template <int DT, bool FWD, bool DQ, bool OUT_F32>
 hipError_t gemm_go(GemmArgs g, hipStream_t s)
 {
-    if constexpr (!FWD) {
-        // 32-bit buffer offsets: 256 rows of x under 2 GiB, codes under 2 GiB
-        if (g.nsplit <= 1 && g.M > 128 && g.kred < (int64_t(1) << 22) && g.kred * g.ncol < (int64_t(1) << 32))
-            return mm_bwd_go<DT, DQ, OUT_F32>(g, s);
-    }
-    if constexpr (FWD) {
-        // 32-bit lane offsets: 256 rows of x (and of codes) under 2 GiB
-        if (g.nsplit <= 1 && g.M > 128 && g.kred < (int64_t(1) << 22)) return mm_fwd_go<DT, DQ, OUT_F32>(g, s);
+    // the 256 x 256 kernels, split as planned by nf4_matmul_splits or whole
+    const bool big = g.nsplit > 1 ? big_splits(FWD, g.M, g.ncol, g.kred) == g.nsplit
+                                  : use_big(FWD, g.M, g.ncol, g.kred);
+    if (big) {
+        if constexpr (FWD) return mm_fwd_go<DT, DQ, OUT_F32>(g, s);
+        else return mm_bwd_go<DT, DQ, OUT_F32>(g, s);
     }
     const int64_t total = g.ntiles * g.nsplit;
     for (int64_t t0 = 0; t0 < total; t0 += kMaxGemmGrid) {
@@ -1233,17 +1303,23 @@ hipError_t gemm_go(GemmArgs g, hipStream_t s)
 
 int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m)
 {
-    // With fewer output tiles than the chip has CUs, each workgroup walks the
-    // whole reduction one dependent k-step after another and the call is bound
-    // by that latency (0.083 ms for any m <= 256 on a 13824 x 5120 weight);
-    // then aim at about 1,024 (tile, split) workgroups, at most 16 splits of
-    // whole k-steps.  Measured on that weight: split at m <= 128 0.038-0.051 ms
-    // forward (dequantise + library GEMM 0.060-0.075), 0.063-0.070 backward
-    // (0.087-0.131); at 432 output tiles and 80 k-steps (m = 512 forward) a
-    // 3-way split was slower than none, at 320 tiles and 216 k-steps (m = 1024
-    // backward) a 4-way split faster (0.327 against 0.477 ms): shapes are split
-    // below 256 tiles, or below 512 when the reduction has 128 k-steps or more.
+    // More than 128 rows of x and too few 256 x 256 tiles for a round: the
+    // large-tile kernels with their reduction split (big_splits).
+    // Where the large-tile kernels take the call whole (use_big): no split.
+    // Otherwise the 128 x 128 kernel: with fewer output tiles than the chip
+    // has CUs, each workgroup walks the whole reduction one dependent k-step
+    // after another and the call is bound by that latency (0.083 ms for any
+    // m <= 256 on a 13824 x 5120 weight); then aim at about 1,024 (tile,
+    // split) workgroups, at most 16 splits of whole k-steps.  Measured on
+    // that weight: split at m <= 128 0.038-0.051 ms forward (dequantise +
+    // library GEMM 0.060-0.075), 0.063-0.070 backward (0.087-0.131); at 432
+    // output tiles and 80 k-steps (m = 512 forward) a 3-way split was slower
+    // than none: shapes are split below 256 tiles, or below 512 when the
+    // reduction has 128 k-steps or more.
     const int64_t kred = forward ? cols : rows, ncol = forward ? rows : cols;
+    const int bsp = big_splits(forward, m, ncol, kred);
+    if (bsp > 0) return bsp;   // the 256 x 256 kernels, split
+    if (use_big(forward, m, ncol, kred)) return 1;   // the 256 x 256 kernels, whole
     const int64_t tiles = ((m + kBM - 1) / kBM) * (ncol / kBN);
     const int64_t ksteps = kred / kBK;
     if (ksteps < 2 || tiles >= 512 || (tiles >= 256 && ksteps < 128)) return 1;

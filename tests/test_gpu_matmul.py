@@ -187,6 +187,30 @@ def test_split_reduction_matches_oracle(m, dtype, backward):
     assert torch.equal(o16, out.to(TORCH16[dtype]))
 
 
+@pytest.mark.parametrize("m", [200, 300])
+@pytest.mark.parametrize("dtype", [BF16, FP16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_split_large_tiles_matches_oracle(backward, dtype, m):
+    """nf4_matmul_ws with more than 128 rows of x and a long reduction over
+    few 256 x 256 tiles: the reduction is split across workgroups of the
+    large-tile kernels (4 splits of 16 k-steps here).  The same bound,
+    bitwise equal from run to run, stale workspace unused, and within the
+    bound too through nf4_matmul, which takes the call unsplit."""
+    rows, cols = (4096, 512) if backward else (512, 4096)
+    ncol = cols if backward else rows
+    print_case("nf4_matmul_ws large tiles split", dtype, m, rows, cols, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 8700 + m + int(backward), True, outliers=0.002, dtype=dtype)
+    xb = _x(m, rows if backward else cols, 19 * m + 3, dtype)
+    out, need = _run_ws(W, xb, backward)
+    assert need == 4 * m * ncol * 4
+    _check(out, xb, W, backward)
+    again, _ = _run_ws(W, xb, backward)
+    assert torch.equal(out, again)
+    o16, _ = _run_ws(W, xb, backward, out_f32=False)
+    assert torch.equal(o16, out.to(TORCH16[dtype]))
+    _check(_run(W, xb, backward), xb, W, backward)
+
+
 # parts of 1 super-chunk (3 and 8 parts), 2 super-chunks with a last part of 1
 # (6 parts), and 2 super-chunks in 10 parts over 68 workgroups of 64 rows
 @pytest.mark.parametrize("shape", [(256, 384), (128, 1024), (8192, 1408), (4352, 2560)],
@@ -220,6 +244,24 @@ def test_split_path_not_taken_equals_nf4_matmul():
     out, need = _run_ws(W, xb, False)
     assert need == 0
     assert torch.equal(out, _run(W, xb, False))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("m", [512, 1536])
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_split_fullsize_ffn_mid_m(backward, m):
+    """The FFN weight at m = 512 and 1536 through nf4_matmul_ws (the
+    large-tile kernels with the reduction split where planned), on sampled
+    rows."""
+    rows, cols = 13824, 5120
+    print_case("nf4_matmul_ws full size mid m", rows, cols, m, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 103, True, outliers=0.0005)
+    xb = _x(m, rows if backward else cols, 104)
+    out, need = _run_ws(W, xb, backward)
+    rng = np.random.default_rng(7)
+    idx = np.sort(np.r_[0, m - 1, rng.integers(0, m, 6)])
+    worst = _check(out, xb, W, backward, rows_idx=idx)
+    print(f"[{'bwd' if backward else 'fwd'} m={m}] worst error / bound {worst:.3f}, workspace {need} B", flush=True)
 
 
 @pytest.mark.slow
