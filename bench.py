@@ -426,10 +426,12 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
                          "achieved": tf(t_bwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tf(t_bwd) / MFMA_BF16_PEAK_TFS, 4)},
     }
-    # few tokens (nf4_matmul_ws: the few-token forward kernel at m <= 32, else
-    # the split reduction) against dequantise + library GEMM
+    # few tokens to mid m (nf4_matmul_ws: the few-token forward kernel at
+    # m <= 32, the split 128 x 128 reduction at m = 128, the 256 x 256
+    # kernels with a split reduction at m = 512) against dequantise + library
+    # GEMM
     small = {}
-    for ms in (16, 32, 128):
+    for ms in (16, 32, 128, 512):
         xs = torch.randn(ms, cols, dtype=torch.bfloat16, device="cuda", generator=gen)
         gs = torch.randn(ms, rows, dtype=torch.bfloat16, device="cuda", generator=gen)
         ysf = torch.empty(ms, rows, dtype=torch.bfloat16, device="cuda")
@@ -448,7 +450,7 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
         small[f"m{ms}"] = {"fused_ws_fwd_ms": round(tf_, 4), "fused_ws_bwd_ms": round(tb_, 4),
                            "fused_ws_fwd_GBps": round(fbytes / (tf_ * 1e-3) / 1e9, 1),
                            "fused_ws_fwd_frac_of_hbm_peak": round(fbytes / (tf_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "library_only_fwd_ms": round(lf, 4),
+                           "library_only_fwd_ms": round(lf, 4), "library_only_bwd_ms": round(lb, 4),
                            "dequant_then_library_fwd_ms": round(t_deq + lf, 4),
                            "dequant_then_library_bwd_ms": round(t_deq + lb, 4)}
         del xs, gs, ysf, ysb, wsf, wsb
