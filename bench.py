@@ -401,9 +401,17 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
     t_deq = deq_ms_per_weight * rows * cols
     w = ls.out_of(li).view(torch.bfloat16).view(rows, cols)   # written by the step's dequant
     wt = w.t().contiguous()
-    t_fwd, t_bwd, t_lib_f, t_lib_b = timed_arms([
+    # nf4_matmul_ws: with a workspace the tiles left over after the whole
+    # rounds split their reduction instead of running as row pieces
+    nwf = q.nf4_matmul_workspace_bytes(rows, cols, False, m)
+    nwb = q.nf4_matmul_workspace_bytes(rows, cols, True, m)
+    wsf = torch.empty(max(nwf, 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(nwb, 1), dtype=torch.uint8, device="cuda")
+    t_fwd, t_bwd, t_wf, t_wb, t_lib_f, t_lib_b = timed_arms([
         lambda: q.nf4_matmul(layer, rows, cols, f, x.view(torch.int16), yf),
         lambda: q.nf4_matmul(layer, rows, cols, f, gy.view(torch.int16), yb, backward=True),
+        lambda: q.nf4_matmul_ws(layer, rows, cols, f, x.view(torch.int16), yf, wsf),
+        lambda: q.nf4_matmul_ws(layer, rows, cols, f, gy.view(torch.int16), yb, wsb, backward=True),
         lambda: torch.matmul(x, wt),
         lambda: torch.matmul(gy, w)])
     flops = 2.0 * m * rows * cols
@@ -419,6 +427,10 @@ def matmul_block(q, torch, ls, f, cfg, stream, deq_ms_per_weight, keep, m=4096, 
         "dequant_then_library_bwd_ms": round(t_deq + t_lib_b, 4),
         "fused_over_dequant_library_fwd": round(t_fwd / (t_deq + t_lib_f), 4),
         "fused_over_dequant_library_bwd": round(t_bwd / (t_deq + t_lib_b), 4),
+        "fused_ws_fwd_ms": round(t_wf, 4), "fused_ws_fwd_TFLOPs": tf(t_wf), "fused_ws_fwd_bytes": nwf,
+        "fused_ws_bwd_ms": round(t_wb, 4), "fused_ws_bwd_TFLOPs": tf(t_wb), "fused_ws_bwd_bytes": nwb,
+        "fused_ws_over_dequant_library_fwd": round(t_wf / (t_deq + t_lib_f), 4),
+        "fused_ws_over_dequant_library_bwd": round(t_wb / (t_deq + t_lib_b), 4),
         "roofline": {"bound": "mfma", "kernel": "nf4_matmul forward",
                      "achieved": tf(t_fwd), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tf(t_fwd) / MFMA_BF16_PEAK_TFS, 4)},

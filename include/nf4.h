@@ -325,7 +325,12 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
  * m <= 32 takes a kernel of its own with the same contract: one wave per 16
  * weight rows and part of the reduction (parts of at most 1024 k, 512 k
  * above 16 tokens), fp32 partials in ws added in part order by the same
- * second kernel. */
+ * second kernel.  Where the output tiles fill the GPU but leave a last round
+ * at most half full (e.g. 4096 tokens through a 13824 x 5120 weight: 320
+ * tiles of 256 x 256 on 256 compute units), the whole rounds run unsplit and
+ * each leftover tile's reduction is split floor(256 / leftover) ways (at most
+ * 16, each part at least 1024 k), into one 256 x 256 fp32 block per (part,
+ * tile) in ws, added in part order into out. */
 nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
                          int32_t backward, const void* x, int64_t m, void* out,
                          int32_t out_fp32, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -333,8 +338,9 @@ nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_for
 /* ---- host-only helpers (pure; no HIP calls) ---- */
 
 /* Workspace of nf4_matmul_ws for this shape: parts * m * (rows | cols) fp32
- * partials rounded up to 256 bytes, or 0 when the shape is not split (its
- * output tiles fill the GPU) or on bad input. */
+ * partials when the whole reduction is split, parts * leftover tiles * 256 *
+ * 256 fp32 when only the leftover tiles' is, rounded up to 256 bytes; 0 when
+ * the shape is not split or on bad input. */
 size_t      nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m);
 
 /* Workspace for every codec call above over these matrices (the descriptor

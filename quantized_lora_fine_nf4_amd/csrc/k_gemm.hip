@@ -127,7 +127,10 @@ struct GemmArgs {
     int64_t nfull, nhalf;   // 256 x 256 tiles: whole tiles, then nhalf tiles split into row pieces (0: none)
     int pieces;             // row pieces of each of those tiles: 2 (128 rows) or 4 (64 rows, backward)
     int split_steps;        // k-steps per split
-    float* part;            // nsplit > 1: fp32 partials [nsplit][M x ncol]
+    float* part;            // nsplit > 1: fp32 partials [nsplit][M x ncol]; tail_split > 0: see there
+    int tail_split;         // 256 x 256 kernels with a workspace: the nhalf tiles from nfull on, each cut
+                            // into tail_split splits of the reduction; partial (split, tile) is one
+                            // 256 x 256 fp32 block at part + (split * nhalf + tile - nfull) * 65536
 };
 
 // Raw constant of W block b as loaded: the int8 and its group scale with
@@ -422,7 +425,8 @@ __device__ __forceinline__ u32x4 deq8_pairs(uint32_t c, float adq, const uint8_t
 // into out (or the fp32 partials of split `split`).  s_mem holds the level
 // table; the x buffers follow it.
 template <int DT, bool DQ, bool OUT_F32, bool PART, int MT>
-__device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split)
+__device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split,
+                                            int64_t poff, int64_t ldp)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, q = lane & 31, h = lane >> 5;
     const uint8_t* lut = s_mem;
@@ -621,7 +625,7 @@ __device__ __forceinline__ void mm_fwd_tile(const GemmArgs& g, uint8_t* s_mem, i
                 const int64_t col = nrow0 + 32 * j;
                 if (full || row < g.M) {
                     if constexpr (PART)
-                        ((GLOBAL float*)g.part)[(int64_t)split * g.M * g.ldo + row * g.ldo + col] = acc[i][j][r];
+                        ((GLOBAL float*)g.part)[poff + row * ldp + col] = acc[i][j][r];
                     else if constexpr (OUT_F32)
                         ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
                     else
@@ -649,6 +653,45 @@ __device__ __forceinline__ int64_t launch_tile(const GemmArgs& g, int& piece)
     return g.nfull + pp / g.pieces;
 }
 
+// What a workgroup of the large-m kernels computes: output tile (mt, nt), row
+// piece (-1: the whole tile), split of the reduction, and with PART where its
+// fp32 partial goes: element (row, col) at part[poff + row * ldp + col].
+struct BigWork {
+    int64_t mt, nt, poff, ldp;
+    int piece, split;
+};
+
+template <bool PART>
+__device__ __forceinline__ BigWork big_work(const GemmArgs& g)
+{
+    BigWork w;
+    int64_t tile;
+    w.piece = -1;
+    w.split = 0;
+    if (PART && g.tail_split > 0) {
+        // the leftover tiles' splits, split outer: each XCD takes a run of
+        // neighbouring tiles of one split (they share rows of x)
+        const int64_t local = xcd_tile(blockIdx.x, gridDim.x);
+        w.split = (int)(local / g.nhalf);
+        tile = g.nfull + (local - (int64_t)w.split * g.nhalf);
+    } else {
+        tile = launch_tile(g, w.piece);
+        if (PART) {
+            w.split = (int)(tile / g.ntiles);
+            tile -= (int64_t)w.split * g.ntiles;
+        }
+    }
+    group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, w.mt, w.nt);
+    w.ldp = g.ldo;
+    w.poff = PART ? (int64_t)w.split * g.M * g.ldo : 0;
+    if (PART && g.tail_split > 0) {
+        // one 256 x 256 block per (split, tile), rows of 256
+        w.ldp = kXN;
+        w.poff = ((int64_t)w.split * g.nhalf + (tile - g.nfull)) * (kXM * kXN) - w.mt * kXM * kXN - w.nt * kXN;
+    }
+    return w;
+}
+
 template <int DT, bool DQ, bool OUT_F32, bool PART>
 __global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
 {
@@ -663,15 +706,12 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_fwd(GemmArgs g)
 #pragma unroll
         for (int c = 0; c < kLutCopies / 2; ++c) row[(c + t) & (kLutCopies / 2 - 1)] = u32x4{lo, hi, lo, hi};
     }
-    int piece;
-    int64_t tile = launch_tile(g, piece);
-    const int split = PART ? (int)(tile / g.ntiles) : 0;
-    if (PART) tile -= (int64_t)split * g.ntiles;
-    int64_t mt, nt;
-    group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
-    if (piece < 0) mm_fwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
-    else if (g.pieces == 2) mm_fwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * piece, nt * kXN, split);
-    else mm_fwd_tile<DT, DQ, OUT_F32, PART, 2>(g, s_mem, mt * kXM + 64 * piece, nt * kXN, split);
+    const BigWork w = big_work<PART>(g);
+    const int64_t m0 = w.mt * kXM, c0 = w.nt * kXN;
+    if (w.piece < 0) mm_fwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, m0, c0, w.split, w.poff, w.ldp);
+    else if (g.pieces == 2)
+        mm_fwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, m0 + 128 * w.piece, c0, w.split, w.poff, w.ldp);
+    else mm_fwd_tile<DT, DQ, OUT_F32, PART, 2>(g, s_mem, m0 + 64 * w.piece, c0, w.split, w.poff, w.ldp);
 }
 
 // ---- large m, backward (input gradient): 256 x 256 output tiles, the weight
@@ -703,7 +743,8 @@ static_assert(kBLds <= 163840, "LDS of one CU");
 __device__ __forceinline__ int wslot(int r, int c) { return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)); }
 
 template <int DT, bool DQ, bool OUT_F32, bool PART, int MT>
-__device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split)
+__device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, int64_t m0, int64_t c0, int split,
+                                            int64_t poff, int64_t ldp)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6, q = lane & 31, h = lane >> 5;
     const uint8_t* lut = s_mem;
@@ -909,7 +950,7 @@ __device__ __forceinline__ void mm_bwd_tile(const GemmArgs& g, uint8_t* s_mem, i
                 const int64_t col = cw + 32 * j + q;
                 if (full || row < g.M) {
                     if constexpr (PART)
-                        ((GLOBAL float*)g.part)[(int64_t)split * g.M * g.ldo + row * g.ldo + col] = acc[i][j][r];
+                        ((GLOBAL float*)g.part)[poff + row * ldp + col] = acc[i][j][r];
                     else if constexpr (OUT_F32)
                         ((GLOBAL float*)g.out)[row * g.ldo + col] = acc[i][j][r];
                     else
@@ -933,15 +974,12 @@ __global__ __launch_bounds__(256, 1) void k_nf4_mm_bwd(GemmArgs g)
     // Each wave dequantises its weight piece whatever the rows, so a 64-row
     // quarter costs more than a quarter of a tile, but the pieces of the last
     // tiles fill one short round.
-    int piece;
-    int64_t tile = launch_tile(g, piece);
-    const int split = PART ? (int)(tile / g.ntiles) : 0;
-    if (PART) tile -= (int64_t)split * g.ntiles;
-    int64_t mt, nt;
-    group_coords(tile, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
-    if (piece < 0) mm_bwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, mt * kXM, nt * kXN, split);
-    else if (g.pieces == 2) mm_bwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, mt * kXM + 128 * piece, nt * kXN, split);
-    else mm_bwd_tile<DT, DQ, OUT_F32, PART, 2>(g, s_mem, mt * kXM + 64 * piece, nt * kXN, split);
+    const BigWork w = big_work<PART>(g);
+    const int64_t m0 = w.mt * kXM, c0 = w.nt * kXN;
+    if (w.piece < 0) mm_bwd_tile<DT, DQ, OUT_F32, PART, 8>(g, s_mem, m0, c0, w.split, w.poff, w.ldp);
+    else if (g.pieces == 2)
+        mm_bwd_tile<DT, DQ, OUT_F32, PART, 4>(g, s_mem, m0 + 128 * w.piece, c0, w.split, w.poff, w.ldp);
+    else mm_bwd_tile<DT, DQ, OUT_F32, PART, 2>(g, s_mem, m0 + 64 * w.piece, c0, w.split, w.poff, w.ldp);
 }
 
 // ---- few tokens, forward: one wave per 16 W rows and one part of the reduction
@@ -1096,6 +1134,32 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float* __restrict__ pa
     }
 }
 
+// The tail splits' fp32 partials of each leftover tile added in split order
+// and stored into out (rows below M, columns below ncol), as fp32 or rounded to
+// the 16-bit type.  Workgroup b covers 1,024 consecutive elements (four per
+// thread, within one row) of the 256 x 256 block of leftover tile b / 64.
+template <int DT, bool OUT_F32>
+__global__ __launch_bounds__(256) void k_tail_sum(GemmArgs g)
+{
+    const int64_t lt = blockIdx.x >> 6;
+    const int e = ((int)(blockIdx.x & 63) << 10) + 4 * (int)threadIdx.x;
+    int64_t mt, nt;
+    group_coords(g.nfull + lt, (g.M + kXM - 1) / kXM, g.ntn, mt, nt);
+    const int64_t row = mt * kXM + (e >> 8), col = nt * kXN + (e & 255);
+    if (row >= g.M || col >= g.ncol) return;   // ncol is a multiple of 128: all four in or all out
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const GLOBAL float* p = (const GLOBAL float*)g.part + lt * (kXM * kXN) + e;
+    f4 acc = *(const GLOBAL f4*)p;
+    for (int sp = 1; sp < g.tail_split; ++sp) acc += *(const GLOBAL f4*)(p + (int64_t)sp * g.nhalf * (kXM * kXN));
+    const int64_t i = row * g.ldo + col;
+    if constexpr (OUT_F32) {
+        *(GLOBAL f4*)((float*)g.out + i) = acc;
+    } else {
+        const u32x2 v = {pack16<DT>(acc.x, acc.y), pack16<DT>(acc.z, acc.w)};
+        *(GLOBAL u32x2*)((uint16_t*)g.out + i) = v;
+    }
+}
+
 // One-shot launches of at most 2^32 / 256 - 1 workgroups each.
 constexpr int64_t kMaxGemmGrid = (int64_t(1) << 32) / kGThreads - 1;
 
@@ -1167,6 +1231,30 @@ int big_splits(bool forward, int64_t M, int64_t ncol, int64_t kred)
     return (int)((ksteps + per - 1) / per);
 }
 
+// With a workspace, the tiles left over after the last whole round of the
+// 256 x 256 kernels (rem of them) run with their reduction split instead of as
+// row pieces: floor(kPlanCus / rem) splits (at most 16, each of at least 16
+// k-steps), so that all their (split, tile) workgroups make one round.  A row
+// piece still dequantises the tile's whole weight slab for fewer MFMAs; a split
+// is a whole tile's work over a part of the reduction, plus its fp32 partial
+// (256 KB written and read back).  0: not taken (no leftover, or more than
+// half a round of it).
+int big_tail_splits(bool forward, int64_t M, int64_t ncol, int64_t kred, int64_t& full, int64_t& rem)
+{
+    if (!use_big(forward, M, ncol, kred)) return 0;
+    const int64_t tiles = ((M + kXM - 1) / kXM) * ((ncol + kXN - 1) / kXN), ksteps = kred / 64;
+    if (tiles <= kPlanCus) return 0;
+    rem = tiles % kPlanCus;
+    full = tiles - rem;
+    if (rem == 0) return 0;
+    int64_t sp = kPlanCus / rem;
+    if (sp > 16) sp = 16;
+    while (sp >= 2 && ksteps / sp < 16) --sp;
+    if (sp < 2) return 0;
+    const int64_t per = (ksteps + sp - 1) / sp;   // whole k-steps per split
+    return (int)((ksteps + per - 1) / per);
+}
+
 // Row pieces for the tiles left over after the last whole round of one
 // workgroup per CU (full whole tiles, rem left over): 64-row quarters when
 // four per tile fit one round, else 128-row halves when two do, each split
@@ -1182,11 +1270,48 @@ int tail_pieces(int64_t total, int64_t ncu, int64_t& full, int64_t& rem)
     return 0;
 }
 
+// The whole tiles unsplit, then the leftover tiles' splits (one launch, one
+// round), then k_tail_sum; all on the caller's stream, in order.
+template <int DT, bool DQ, bool OUT_F32, bool FWD>
+hipError_t big_tail_go(GemmArgs g, hipStream_t s)
+{
+    int64_t full = 0, rem = 0;
+    if (big_tail_splits(FWD, g.M, g.ncol, g.kred, full, rem) != g.tail_split) return hipErrorInvalidValue;
+    const int ksteps = (int)(g.kred / 64);
+    g.nsplit = 1;
+    g.nhalf = 0;
+    g.pieces = 2;
+    for (int64_t t0 = 0; t0 < full; t0 += kMaxGemmGrid) {
+        const int64_t n = full - t0 < kMaxGemmGrid ? full - t0 : kMaxGemmGrid;
+        g.tile0 = t0;
+        if constexpr (FWD)
+            hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, false>), dim3((unsigned)n), dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((k_nf4_mm_bwd<DT, DQ, OUT_F32, false>), dim3((unsigned)n), dim3(256), 0, s, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    g.tile0 = 0;
+    g.nfull = full;
+    g.nhalf = rem;
+    g.split_steps = (ksteps + g.tail_split - 1) / g.tail_split;
+    const unsigned grid = (unsigned)(rem * g.tail_split);
+    if constexpr (FWD)
+        hipLaunchKernelGGL((k_nf4_mm_fwd<DT, DQ, OUT_F32, true>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((k_nf4_mm_bwd<DT, DQ, OUT_F32, true>), dim3(grid), dim3(256), 0, s, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_tail_sum<DT, OUT_F32>), dim3((unsigned)(rem * 64)), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
 template <int DT, bool DQ, bool OUT_F32>
 hipError_t mm_fwd_go(GemmArgs g, hipStream_t s)
 {
     g.ntn = (g.ncol + kXN - 1) / kXN;
     g.ntiles = ((g.M + kXM - 1) / kXM) * g.ntn;
+    if (g.tail_split > 0) return big_tail_go<DT, DQ, OUT_F32, true>(g, s);
     const int64_t total = g.ntiles * g.nsplit;
     // With one workgroup per CU, the tiles past the last whole round run in
     // row pieces when those fit one round.
@@ -1230,6 +1355,7 @@ hipError_t mm_bwd_go(GemmArgs g, hipStream_t s)
 {
     g.ntn = (g.ncol + kXN - 1) / kXN;
     g.ntiles = ((g.M + kXM - 1) / kXM) * g.ntn;
+    if (g.tail_split > 0) return big_tail_go<DT, DQ, OUT_F32, false>(g, s);
     g.nfull = g.ntiles;
     g.nhalf = 0;
     g.tile0 = 0;
@@ -1330,6 +1456,17 @@ int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m)
     return (int)((ksteps + per - 1) / per);
 }
 
+int nf4_matmul_tail_splits(int64_t rows, int64_t cols, bool forward, int64_t m, int64_t* rem_out)
+{
+    // only where the 256 x 256 kernels take the call whole (no split planned)
+    const int64_t kred = forward ? cols : rows, ncol = forward ? rows : cols;
+    if (nf4_matmul_splits(rows, cols, forward, m) != 1) return 0;
+    int64_t full = 0, rem = 0;
+    const int sp = big_tail_splits(forward, m, ncol, kred, full, rem);
+    if (sp > 0 && rem_out) *rem_out = rem;
+    return sp;
+}
+
 namespace {
 
 // Super-chunks per part: about 2,048 (row group, part) waves, at most
@@ -1402,7 +1539,7 @@ hipError_t launch_nf4_gemv(int dtype, const uint8_t* codes, const int8_t* qabsma
 hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
                              const float* absmax, int64_t rows, int64_t cols, bool forward,
                              const void* x, int64_t m, void* out, bool out_f32, float* part, int nsplit,
-                             hipStream_t s)
+                             int tail_split, hipStream_t s)
 {
     GemmArgs g;
     g.a = static_cast<const uint16_t*>(x);
@@ -1427,6 +1564,7 @@ hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabs
     g.nsplit = (part && nsplit > 1) ? nsplit : 1;
     g.split_steps = (ksteps + g.nsplit - 1) / g.nsplit;
     g.part = part;
+    g.tail_split = (part && g.nsplit == 1 && tail_split > 1) ? tail_split : 0;
     const bool dq = qabsmax != nullptr;
 #define NF4_GEMM(T, F, D, O) return gemm_go<T, F, D, O>(g, s)
 #define NF4_GEMM_DT(T)                                                                             \

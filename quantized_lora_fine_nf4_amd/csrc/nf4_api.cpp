@@ -229,13 +229,13 @@ nf4_status check_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_form
 
 nf4_status run_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt, int32_t backward,
                       const void* x, int64_t m, void* out, int32_t out_fp32, float* part, int nsplit,
-                      hipStream_t stream)
+                      int tail_split, hipStream_t stream)
 {
     const bool dq = fmt.dq_group != 0;
     hipError_t e = nf4k::launch_nf4_matmul(fmt.dtype, w->codes, dq ? w->qabsmax : nullptr,
                                            dq ? w->scale2 : nullptr, dq ? nullptr : w->absmax,
                                            rows, cols, backward == 0, x, m, out, out_fp32 == 1,
-                                           part, nsplit, stream);
+                                           part, nsplit, tail_split, stream);
     return e == hipSuccess ? NF4_OK : hip_fail(e);
 }
 
@@ -245,6 +245,17 @@ size_t matmul_part_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m
     if (nsplit <= 1) return 0;
     const int64_t ncol = backward ? cols : rows;
     return align256(size_t(nsplit) * size_t(m) * size_t(ncol) * sizeof(float));
+}
+
+// Bytes of fp32 partials of the leftover tiles' splits: one 256 x 256 block per
+// (split, tile); 0 when the shape has no such split.
+size_t matmul_tail_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m, int* tail_split)
+{
+    int64_t rem = 0;
+    const int ts = nf4k::nf4_matmul_tail_splits(rows, cols, backward == 0, m, &rem);
+    if (tail_split) *tail_split = ts;
+    if (ts <= 1) return 0;
+    return align256(size_t(ts) * size_t(rem) * size_t(256 * 256) * sizeof(float));
 }
 
 }  // namespace
@@ -467,7 +478,7 @@ nf4_status nf4_matmul(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format
 {
     nf4_status st = check_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32);
     if (st != NF4_OK) return st;
-    return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, nullptr, 1, stream);
+    return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, nullptr, 1, 0, stream);
 }
 
 size_t nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m)
@@ -477,7 +488,8 @@ size_t nf4_matmul_workspace_bytes(int64_t rows, int64_t cols, int32_t backward, 
     if (rows > kMaxN / cols || (backward != 0 && backward != 1)) return 0;
     const int gv = nf4k::nf4_gemv_parts(rows, cols, backward == 0, m);
     if (gv > 0) return align256(size_t(gv) * size_t(m) * size_t(rows) * sizeof(float));
-    return matmul_part_bytes(rows, cols, backward, m, nf4k::nf4_matmul_splits(rows, cols, backward == 0, m));
+    const size_t split = matmul_part_bytes(rows, cols, backward, m, nf4k::nf4_matmul_splits(rows, cols, backward == 0, m));
+    return split > 0 ? split : matmul_tail_bytes(rows, cols, backward, m, nullptr);
 }
 
 nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_format fmt,
@@ -499,11 +511,19 @@ nf4_status nf4_matmul_ws(const nf4_layer* w, int64_t rows, int64_t cols, nf4_for
     }
     const int nsplit = nf4k::nf4_matmul_splits(rows, cols, backward == 0, m);
     const size_t need = matmul_part_bytes(rows, cols, backward, m, nsplit);
-    if (need == 0)
-        return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, nullptr, 1, stream);
+    if (need == 0) {
+        int tail = 0;
+        const size_t tneed = matmul_tail_bytes(rows, cols, backward, m, &tail);
+        if (tneed == 0)
+            return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, nullptr, 1, 0, stream);
+        st = check_ws(ws, ws_bytes, tneed);
+        if (st != NF4_OK) return st;
+        return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, static_cast<float*>(ws), 1, tail,
+                          stream);
+    }
     st = check_ws(ws, ws_bytes, need);
     if (st != NF4_OK) return st;
-    return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, static_cast<float*>(ws), nsplit,
+    return run_matmul(w, rows, cols, fmt, backward, x, m, out, out_fp32, static_cast<float*>(ws), nsplit, 0,
                       stream);
 }
 

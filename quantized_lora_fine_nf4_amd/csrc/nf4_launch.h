@@ -45,14 +45,22 @@ hipError_t launch_variant_dequant(const LayerDesc* tab, int nl, int64_t ngroups,
 // multiples of 128; x and the dequantised W in the 16-bit type dtype (0 bf16,
 // 1 fp16); out fp32 or that 16-bit type.  With part != nullptr and nsplit > 1
 // the reduction is split nsplit ways into fp32 partials at part
-// ([nsplit][m x (rows | cols)]), then added in split order into out.
+// ([nsplit][m x (rows | cols)]), then added in split order into out.  With
+// part != nullptr, nsplit == 1 and tail_split > 1 (the value
+// nf4_matmul_tail_splits gives for the shape), the tiles left over after the
+// whole rounds are split tail_split ways into [tail_split][rem][256 x 256]
+// fp32 blocks at part, then added in split order into out.
 hipError_t launch_nf4_matmul(int dtype, const uint8_t* codes, const int8_t* qabsmax, const float* scale2,
                              const float* absmax, int64_t rows, int64_t cols, bool forward,
                              const void* x, int64_t m, void* out, bool out_f32, float* part, int nsplit,
-                             hipStream_t s);
+                             int tail_split, hipStream_t s);
 // The split count the split-reduction matmul uses for a shape (1: none); a
 // function of the shape only.
 int nf4_matmul_splits(int64_t rows, int64_t cols, bool forward, int64_t m);
+// Where the large-tile kernels take a shape whole: the split count of its
+// leftover tiles with a workspace (0: none) and, when > 0, their number in
+// *rem_out; a function of the shape only.
+int nf4_matmul_tail_splits(int64_t rows, int64_t cols, bool forward, int64_t m, int64_t* rem_out);
 // Few-token forward (m <= 32): the part count of the wave-per-16-rows path
 // (0 when it does not apply); a function of the shape only.
 int nf4_gemv_parts(int64_t rows, int64_t cols, bool forward, int64_t m);

@@ -302,7 +302,23 @@ def test_matmul_split_workspace_and_arguments():
         assert w16 > 0 and w16 % 256 == 0 and w16 % (16 * ncol * 4) == 0
         parts = w16 // (16 * ncol * 4)
         assert 2 <= parts <= 16
-        assert q.nf4_matmul_workspace_bytes(rows, cols, backward, 4096) == 0
+    # m = 4096: 864 (forward) or 320 (backward) tiles of 256 x 256 on 256 CUs;
+    # the 96 or 64 leftover tiles' reductions split 2 or 4 ways, one 256 x 256
+    # fp32 block per (split, tile)
+    assert q.nf4_matmul_workspace_bytes(rows, cols, 0, 4096) == 2 * 96 * 256 * 256 * 4
+    assert q.nf4_matmul_workspace_bytes(rows, cols, 1, 4096) == 4 * 64 * 256 * 256 * 4
+    # whole rounds only (4096 x 4096, m = 4096: 256 tiles): no workspace
+    assert q.nf4_matmul_workspace_bytes(4096, 4096, 0, 4096) == 0
+    # the parity test's shapes: 320 tiles (ragged rows, a 128-column tail), 4 splits
+    # of 16 k-steps; 352 tiles, 2 splits of 16 k-steps
+    assert q.nf4_matmul_workspace_bytes(4992, 4096, 0, 3900) == 4 * 64 * 256 * 256 * 4
+    assert q.nf4_matmul_workspace_bytes(4096, 4992, 1, 3900) == 4 * 64 * 256 * 256 * 4
+    assert q.nf4_matmul_workspace_bytes(5632, 2048, 0, 4096) == 2 * 96 * 256 * 256 * 4
+    assert q.nf4_matmul_workspace_bytes(2048, 5632, 1, 4096) == 2 * 96 * 256 * 256 * 4
+    # more than half a round left over (400 tiles: 144 left) or a reduction too
+    # short to split (16 k-steps): none
+    assert q.nf4_matmul_workspace_bytes(6400, 4096, 0, 4096) == 0
+    assert q.nf4_matmul_workspace_bytes(4992, 1024, 0, 3900) == 0
     assert q.nf4_matmul_workspace_bytes(rows, cols, 0, 0) == 0
     assert q.nf4_matmul_workspace_bytes(200, cols, 0, 16) == 0
     assert L.nf4_matmul_workspace_bytes(rows, cols, 2, 16) == 0

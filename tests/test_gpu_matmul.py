@@ -9,7 +9,8 @@ fp16, ragged m (1, 77, 300), several tile counts, double quant on and off,
 forward and backward; a shape whose last tiles run as halves, every element;
 the 14B stack's FFN shape (13824 x 5120) at m = 4096 on sampled rows.  The split-reduction path (nf4_matmul_ws) on shapes it
 splits, against the same bound, deterministic, and the FFN shape at m = 16
-and 32; its few-token forward kernel (m <= 32: 1, 5, 16, 17, 32) the same way.
+and 32; its split of the tiles left over after whole rounds (two shapes, and
+the FFN shape at m = 4096); its few-token forward kernel (m <= 32: 1, 5, 16, 17, 32) the same way.
 """
 import numpy as np
 import pytest
@@ -211,6 +212,36 @@ def test_split_large_tiles_matches_oracle(backward, dtype, m):
     _check(_run(W, xb, backward), xb, W, backward)
 
 
+@pytest.mark.parametrize("case", [(3900, 4992, 4096, 4), (4096, 5632, 2048, 2)],
+                         ids=["320tiles-4splits", "352tiles-2splits"])
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_tail_split_matches_oracle(backward, case):
+    """nf4_matmul_ws where the 256 x 256 tiles fill whole rounds and leave
+    fewer than half a round over: the whole tiles run unsplit, the leftover
+    tiles' reductions split (4 ways over 64 tiles, 2 ways over 96) into one
+    fp32 block per (split, tile), added in split order.  The first shape has a
+    ragged last row tile (60 rows) and a 128-column last column tile, both
+    among the leftover tiles.  Checked on every row of the last four row tiles
+    (which hold all the leftover tiles and some whole ones) and sampled rows
+    above: the same fp32 bound, 16-bit output = RNE of its fp32 output,
+    bitwise equal from run to run, stale workspace unused."""
+    m, ncol, kred, splits = case
+    rows, cols = (kred, ncol) if backward else (ncol, kred)
+    print_case("nf4_matmul_ws tail split", m, rows, cols, "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 8900 + m + int(backward), True, outliers=0.001)
+    xb = _x(m, kred, 23 * m + int(backward))
+    out, need = _run_ws(W, xb, backward)
+    tiles = -(-m // 256) * -(-ncol // 256)
+    assert need == splits * (tiles - 256) * 256 * 256 * 4
+    rng = np.random.default_rng(m)
+    idx = np.unique(np.r_[np.arange(3072, m), 0, 255, 256, rng.integers(0, 3072, 8)])
+    _check(out, xb, W, backward, rows_idx=idx)
+    again, _ = _run_ws(W, xb, backward)
+    assert torch.equal(out, again)
+    o16, _ = _run_ws(W, xb, backward, out_f32=False)
+    assert torch.equal(o16, out.to(torch.bfloat16))
+
+
 # parts of 1 super-chunk (3 and 8 parts), 2 super-chunks with a last part of 1
 # (6 parts), and 2 super-chunks in 10 parts over 68 workgroups of 64 rows
 @pytest.mark.parametrize("shape", [(256, 384), (128, 1024), (8192, 1408), (4352, 2560)],
@@ -247,11 +278,12 @@ def test_split_path_not_taken_equals_nf4_matmul():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("m", [512, 1536])
+@pytest.mark.parametrize("m", [512, 1536, 4096])
 @pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
 def test_split_fullsize_ffn_mid_m(backward, m):
     """The FFN weight at m = 512 and 1536 through nf4_matmul_ws (the
-    large-tile kernels with the reduction split where planned), on sampled
+    large-tile kernels with the reduction split where planned), and at
+    m = 4096 (whole rounds unsplit, the leftover tiles split), on sampled
     rows."""
     rows, cols = 13824, 5120
     print_case("nf4_matmul_ws full size mid m", rows, cols, m, "bwd" if backward else "fwd")
@@ -259,7 +291,8 @@ def test_split_fullsize_ffn_mid_m(backward, m):
     xb = _x(m, rows if backward else cols, 104)
     out, need = _run_ws(W, xb, backward)
     rng = np.random.default_rng(7)
-    idx = np.sort(np.r_[0, m - 1, rng.integers(0, m, 6)])
+    # at m = 4096 the leftover tiles hold rows 3072 .. 4095
+    idx = np.unique(np.r_[0, m - 1, rng.integers(0, m, 6), rng.integers(max(0, m - 1024), m, 4)])
     worst = _check(out, xb, W, backward, rows_idx=idx)
     print(f"[{'bwd' if backward else 'fwd'} m={m}] worst error / bound {worst:.3f}, workspace {need} B", flush=True)
 
