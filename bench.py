@@ -507,6 +507,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="14b", help="toy | single | 1.4b | 7b | 14b")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--warm-seconds", type=float, default=0.0,
+                    help="after the W warmup steps, keep stepping untimed for this long (the clock "
+                         "settles only under sustained load; matters for the small stacks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the selection variants, the fused matmul and the codec variants")
@@ -594,6 +597,13 @@ def main():
     for _ in range(args.warmup):
         keep = step()
     torch.cuda.synchronize()
+    if args.warm_seconds > 0:
+        # small stacks: W steps last a few ms, less than the GPU needs to reach
+        # its sustained clock (a 1.4B fused pass takes 0.63 ms cold, 0.54 warm)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.warm_seconds:
+            keep = step()
+        torch.cuda.synchronize()
 
     K = args.steps
     evs = [{"fused": [torch.cuda.Event(enable_timing=True) for _ in range(2)],
@@ -651,6 +661,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        **({"warm_seconds": args.warm_seconds} if args.warm_seconds > 0 else {}),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
