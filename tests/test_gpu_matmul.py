@@ -212,24 +212,28 @@ def test_split_large_tiles_matches_oracle(backward, dtype, m):
     _check(_run(W, xb, backward), xb, W, backward)
 
 
-@pytest.mark.parametrize("case", [(3900, 4992, 4096, 4), (4096, 5632, 2048, 2)],
-                         ids=["320tiles-4splits", "352tiles-2splits"])
+@pytest.mark.parametrize("case,dtype,dq", [((3900, 4992, 4096, 4), BF16, True),
+                                           ((4096, 5632, 2048, 2), BF16, True),
+                                           ((3900, 4992, 4096, 4), FP16, False)],
+                         ids=["320tiles-4splits", "352tiles-2splits", "320tiles-fp16-nodq"])
 @pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
-def test_tail_split_matches_oracle(backward, case):
+def test_tail_split_matches_oracle(backward, case, dtype, dq):
     """nf4_matmul_ws where the 256 x 256 tiles fill whole rounds and leave
     fewer than half a round over: the whole tiles run unsplit, the leftover
     tiles' reductions split (4 ways over 64 tiles, 2 ways over 96) into one
     fp32 block per (split, tile), added in split order.  The first shape has a
     ragged last row tile (60 rows) and a 128-column last column tile, both
-    among the leftover tiles.  Checked on every row of the last four row tiles
+    among the leftover tiles; it runs in bf16 with double quant and in fp16
+    with fp32 absmax.  Checked on every row of the last four row tiles
     (which hold all the leftover tiles and some whole ones) and sampled rows
     above: the same fp32 bound, 16-bit output = RNE of its fp32 output,
     bitwise equal from run to run, stale workspace unused."""
     m, ncol, kred, splits = case
     rows, cols = (kred, ncol) if backward else (ncol, kred)
-    print_case("nf4_matmul_ws tail split", m, rows, cols, "bwd" if backward else "fwd")
-    W = DevWeight(rows, cols, 8900 + m + int(backward), True, outliers=0.001)
-    xb = _x(m, kred, 23 * m + int(backward))
+    print_case("nf4_matmul_ws tail split", m, rows, cols, dtype, "dq" if dq else "nodq",
+               "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 8900 + m + int(backward), dq, outliers=0.001, dtype=dtype)
+    xb = _x(m, kred, 23 * m + int(backward), dtype)
     out, need = _run_ws(W, xb, backward)
     tiles = -(-m // 256) * -(-ncol // 256)
     assert need == splits * (tiles - 256) * 256 * 256 * 4
@@ -239,7 +243,7 @@ def test_tail_split_matches_oracle(backward, case):
     again, _ = _run_ws(W, xb, backward)
     assert torch.equal(out, again)
     o16, _ = _run_ws(W, xb, backward, out_f32=False)
-    assert torch.equal(o16, out.to(torch.bfloat16))
+    assert torch.equal(o16, out.to(TORCH16[dtype]))
 
 
 # parts of 1 super-chunk (3 and 8 parts), 2 super-chunks with a last part of 1
