@@ -19,7 +19,10 @@
 //     (k_nf4_mm_fwd: the weight fragments dequantised straight into MFMA
 //     registers; k_nf4_mm_bwd: each wave's weight piece transposed through LDS
 //     with the transposing read).  Tiles left over after the last whole round
-//     run as 64-row quarters, or 128-row halves, when those fit one round.
+//     run as 64-row quarters, or 128-row halves, when those fit one round;
+//     with a workspace their reduction is split instead (fp32 partial blocks
+//     added in split order by k_tail_sum), and with few tiles and a workspace
+//     every tile's reduction is split (k_splitk_sum adds the splits).
 //   * m <= 128 (and any split reduction): k_nf4_matmul, 128 x 128 tiles, three
 //     workgroups per CU, the weight tile dequantised into LDS (transposed on
 //     the way backward).
