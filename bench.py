@@ -573,8 +573,6 @@ def main():
     sws = torch.empty(q.aqlora_workspace_bytes(nl), dtype=torch.uint8, device="cuda")
     budget = cfg.budgets_bytes()[0] if cfg.budgets_gib else -1
     stream = torch.cuda.current_stream()
-    subsets = {}
-
     def step(events=None):
         if events is not None:
             events["fused"][0].record(stream)
@@ -582,28 +580,28 @@ def main():
         if events is not None:
             events["fused"][1].record(stream)
         q.aqlora_select_topk(err, cost, budget, cfg.kcap, sel, kout, sws)
-        keep = tuple(i for i, s in enumerate(sel.cpu().tolist()) if not s)   # synchronises
-        sub = subsets.get(keep)
-        if sub is None:
-            sub = subsets[keep] = ls.subset(keep)
+        # the promoted matrices skip dequantisation: the selection stays on the
+        # device as the mask, no host round trip inside the step
         for r in range(cfg.dequant_repeats):
             if events is not None:
                 events["dequant"][2 * r].record(stream)
-            q.nf4_dequantize(sub, f, ws)
+            q.nf4_dequantize_masked(ls, f, sel, ws)
             if events is not None:
                 events["dequant"][2 * r + 1].record(stream)
-        return keep
+
+    def selected_keep():
+        return tuple(i for i, s in enumerate(sel.cpu().tolist()) if not s)   # synchronises
 
     for _ in range(args.warmup):
-        keep = step()
+        step()
     torch.cuda.synchronize()
     if args.warm_seconds > 0:
         # small stacks: W steps last a few ms, less than the GPU needs to reach
         # its sustained clock (a 1.4B fused pass takes 0.63 ms cold, 0.54 warm)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < args.warm_seconds:
-            keep = step()
-        torch.cuda.synchronize()
+            step()
+            torch.cuda.synchronize()
 
     K = args.steps
     evs = [{"fused": [torch.cuda.Event(enable_timing=True) for _ in range(2)],
@@ -612,7 +610,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        keep = step(evs[s])
+        step(evs[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -622,6 +620,7 @@ def main():
               for e in evs for r in range(cfg.dequant_repeats)]
     deq_ms = sum(deq_ms) / max(1, len(deq_ms))
 
+    keep = selected_keep()   # the same every step (deterministic); read after the timed region
     n_deq = sum(cfg.sizes[i] for i in keep)
     bpw = algorithmic_bytes_per_weight(cfg.dq)
     fused_bytes = bpw * n_total
@@ -687,7 +686,7 @@ def main():
             r % 128 == 0 and c % 128 == 0 for _, r, c in cfg.per_block):
         out["matmul"] = matmul_block(q, torch, ls, f, cfg, stream, deq_ms / max(1, n_deq), set(keep))
     if args.protocol > 0:
-        sub = subsets[keep]
+        sub = ls.subset(keep)
         out["protocol"] = {
             "seconds_per_arm": args.protocol,
             "nf4_layer_error": protocol_arms(lambda: q.nf4_layer_error(ls, f, err, ws),

@@ -85,7 +85,7 @@ extern "C" {
  * this header needs no HIP include. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define NF4_ABI_VERSION 4
+#define NF4_ABI_VERSION 5
 
 typedef enum {
     NF4_OK = 0,
@@ -167,6 +167,20 @@ nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt,
  * superset, is enough). */
 nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* nf4_dequantize of the matrices a selection left in NF4 form, with the
+ * selection on the device: matrix i is dequantised iff skip[i] == 0, and the
+ * out buffer of a matrix with skip[i] != 0 is not touched.  Passing
+ * aqlora_select_topk's (or aqlora_select's) `selected` array as skip gives
+ * AQLoRA's step: the promoted matrices keep their 16-bit weights and skip
+ * dequantisation (AQLoRA listing, English abstract), with no host round trip
+ * between the selection and the dequantisation.  skip: device uint8[nl], read
+ * in stream order (NULL: NF4_E_ARG).  Every matrix needs its out pointer and
+ * constants as for nf4_dequantize; ws as for nf4_dequantize over all nl
+ * matrices. */
+nf4_status nf4_dequantize_masked(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                                 const uint8_t* skip, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /* The fused single pass: quantise (+ double-quantise), dequantise in
  * registers with the constants the user gets back, and score each matrix by

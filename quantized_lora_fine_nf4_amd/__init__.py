@@ -6,8 +6,8 @@ codec and of the ranking runs in the HIP kernels.  PyTorch provides device
 memory and the current stream; nothing here computes on the CPU, and a
 missing library raises instead of falling back.
 
-    nf4_quantize, nf4_double_quant, nf4_dequantize, nf4_layer_error,
-    aqlora_select_topk                      -- enqueue on the current stream
+    nf4_quantize, nf4_double_quant, nf4_dequantize, nf4_dequantize_masked,
+    nf4_layer_error, aqlora_select_topk     -- enqueue on the current stream
     nf4_workspace_bytes, aqlora_workspace_bytes, nf4_storage_bytes,
     aqlora_promote_cost, nf4_levels, nf4_thresholds, nf4_abi_version
                                             -- host-only helpers
@@ -69,6 +69,9 @@ EXPORTS = {
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nf4_dequantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "nf4_dequantize_masked": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p]),
     "nf4_layer_error": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, nf4_format,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]),
@@ -187,6 +190,14 @@ def nf4_dequantize(layers, f: nf4_format, ws, stream=None) -> None:
     arr, nl = _layers_arg(layers)
     _check(lib().nf4_dequantize(arr, nl, f, _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "nf4_dequantize")
+
+
+def nf4_dequantize_masked(layers, f: nf4_format, skip, ws, stream=None) -> None:
+    """nf4_dequantize of the layers whose byte in skip (device uint8[nl], e.g.
+    aqlora_select_topk's selected) is 0; the others' outputs are untouched."""
+    arr, nl = _layers_arg(layers)
+    _check(lib().nf4_dequantize_masked(arr, nl, f, _ptr(skip), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "nf4_dequantize_masked")
 
 
 def nf4_layer_error(layers, f: nf4_format, err, ws, stream=None) -> None:

@@ -870,10 +870,14 @@ struct alignas(32) DqTile {
 };
 static_assert(sizeof(DqTile) == kPartsPerTile * sizeof(double), "a record fits a tile's partials");
 
-// One thread per tile: find the layer (binary search over tile_end), write the record.
+// One thread per tile: find the layer (binary search over tile_end), write the
+// record.  skip (device, one byte per layer, may be null): a layer with a
+// nonzero byte gets valid = 0 in every record, so its units do nothing and its
+// output is not touched.
 template <bool DQ>
 __global__ __launch_bounds__(kThreads) void k_dq_prep(const LayerDesc* __restrict__ tab, int nl,
-                                                      int64_t ntiles, DqTile* __restrict__ desc)
+                                                      int64_t ntiles, const uint8_t* __restrict__ skip,
+                                                      DqTile* __restrict__ desc)
 {
     const int64_t tile = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (tile >= ntiles) return;
@@ -893,6 +897,7 @@ __global__ __launch_bounds__(kThreads) void k_dq_prep(const LayerDesc* __restric
         r.s2 = 0.0f;
     }
     r.valid = rem < kTileElems ? (int32_t)rem : kTileElems;
+    if (skip && skip[l]) r.valid = 0;
     desc[tile] = r;
 }
 
@@ -1112,12 +1117,13 @@ hipError_t codec_go(const LayerDesc* tab, int nl, int64_t ntiles, bool ragged, v
 }
 
 template <int DT, bool DQ>
-hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, void* desc_ws, hipStream_t s)
+hipError_t dequant_go(const LayerDesc* tab, int nl, int64_t ntiles, const uint8_t* skip, void* desc_ws,
+                      hipStream_t s)
 {
     DqTile* desc = static_cast<DqTile*>(desc_ws);
     if (ntiles > kMaxGrid * kThreads) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_dq_prep<DQ>), dim3((unsigned)((ntiles + kThreads - 1) / kThreads)), dim3(kThreads),
-                       0, s, tab, nl, ntiles, desc);
+                       0, s, tab, nl, ntiles, skip, desc);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
     const int64_t nunits = ntiles * kDqSplit;
@@ -1156,12 +1162,12 @@ hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, do
 }
 
 hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                          void* desc_ws, hipStream_t s)
+                          const uint8_t* skip, void* desc_ws, hipStream_t s)
 {
-    if (dtype == 0) return dq ? dequant_go<0, true>(tab, nl, ntiles, desc_ws, s)
-                              : dequant_go<0, false>(tab, nl, ntiles, desc_ws, s);
-    return dq ? dequant_go<1, true>(tab, nl, ntiles, desc_ws, s)
-              : dequant_go<1, false>(tab, nl, ntiles, desc_ws, s);
+    if (dtype == 0) return dq ? dequant_go<0, true>(tab, nl, ntiles, skip, desc_ws, s)
+                              : dequant_go<0, false>(tab, nl, ntiles, skip, desc_ws, s);
+    return dq ? dequant_go<1, true>(tab, nl, ntiles, skip, desc_ws, s)
+              : dequant_go<1, false>(tab, nl, ntiles, skip, desc_ws, s);
 }
 
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)

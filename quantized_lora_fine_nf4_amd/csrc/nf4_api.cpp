@@ -258,6 +258,26 @@ size_t matmul_tail_bytes(int64_t rows, int64_t cols, int32_t backward, int64_t m
     return align256(size_t(ts) * size_t(rem) * size_t(256 * 256) * sizeof(float));
 }
 
+// nf4_dequantize, with the device skip mask of nf4_dequantize_masked (or null).
+nf4_status dequantize_impl(const nf4_layer* layers, int32_t nl, nf4_format fmt, const uint8_t* skip,
+                           void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    nf4_status st = check_format(fmt);
+    if (st != NF4_OK) return st;
+    const bool dq = fmt.dq_group != 0;
+    int64_t ntiles = 0;
+    st = check_layers(layers, nl, NEED_CODES | NEED_OUT | (dq ? NEED_Q | NEED_S2 : NEED_ABSMAX),
+                      &ntiles);
+    if (st != NF4_OK) return st;
+    // the table, then one 32-byte record per tile (where the fused pass keeps its partials)
+    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + partial_bytes(ntiles))) != NF4_OK) return st;
+    hipStream_t s = stream;
+    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
+    hipError_t e = nf4k::launch_dequant(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype,
+                                        dq, skip, static_cast<char*>(ws) + table_bytes(nl), s);
+    return e == hipSuccess ? NF4_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,20 +379,14 @@ nf4_status nf4_double_quant(const nf4_layer* layers, int32_t nl, nf4_format fmt,
 nf4_status nf4_dequantize(const nf4_layer* layers, int32_t nl, nf4_format fmt, void* ws,
                           size_t ws_bytes, hipStream_t stream)
 {
-    nf4_status st = check_format(fmt);
-    if (st != NF4_OK) return st;
-    const bool dq = fmt.dq_group != 0;
-    int64_t ntiles = 0;
-    st = check_layers(layers, nl, NEED_CODES | NEED_OUT | (dq ? NEED_Q | NEED_S2 : NEED_ABSMAX),
-                      &ntiles);
-    if (st != NF4_OK) return st;
-    // the table, then one 32-byte record per tile (where the fused pass keeps its partials)
-    if ((st = check_ws(ws, ws_bytes, table_bytes(nl) + partial_bytes(ntiles))) != NF4_OK) return st;
-    hipStream_t s = stream;
-    if ((st = stage_table(layers, nl, ws, s)) != NF4_OK) return st;
-    hipError_t e = nf4k::launch_dequant(static_cast<const LayerDesc*>(ws), nl, ntiles, fmt.dtype,
-                                        dq, static_cast<char*>(ws) + table_bytes(nl), s);
-    return e == hipSuccess ? NF4_OK : hip_fail(e);
+    return dequantize_impl(layers, nl, fmt, nullptr, ws, ws_bytes, stream);
+}
+
+nf4_status nf4_dequantize_masked(const nf4_layer* layers, int32_t nl, nf4_format fmt,
+                                 const uint8_t* skip, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!skip) return NF4_E_ARG;
+    return dequantize_impl(layers, nl, fmt, skip, ws, ws_bytes, stream);
 }
 
 nf4_status nf4_layer_error(const nf4_layer* layers, int32_t nl, nf4_format fmt, double* err,

@@ -22,9 +22,10 @@ hipError_t launch_codec(const LayerDesc* tab, int nl, int64_t ntiles, bool ragge
 hipError_t launch_reduce(const LayerDesc* tab, int nl, const double* partial, double* err,
                          hipStream_t s);
 // Standalone dequantisation (qabsmax/scale2 when dq, else absmax); desc_ws:
-// device scratch for one 32-byte record per tile (kPartsPerTile doubles).
+// device scratch for one 32-byte record per tile (kPartsPerTile doubles);
+// skip: null, or device uint8[nl] (layers with a nonzero byte are left alone).
 hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtype, bool dq,
-                          void* desc_ws, hipStream_t s);
+                          const uint8_t* skip, void* desc_ws, hipStream_t s);
 // Standalone double quantisation of absmax.
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s);
 // Budgeted top-K; rank/perm are int32[nl] workspace arrays.

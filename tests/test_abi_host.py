@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(q.EXPORTS), set(names) ^ set(q.EXPORTS)
-    assert q.nf4_abi_version() == 4
+    assert q.nf4_abi_version() == 5
 
 
 def test_embedded_levels_and_thresholds_equal_the_oracles():
@@ -73,15 +73,17 @@ def _L(n=128, w=FAKE, codes=FAKE, absmax=FAKE, qabsmax=FAKE, scale2=FAKE, out=FA
     return q.nf4_layer(n, w, codes, absmax, qabsmax, scale2, out)
 
 
-def _call(name, layers, f, ws=FAKE, ws_bytes=1 << 20, err=FAKE):
+def _call(name, layers, f, ws=FAKE, ws_bytes=1 << 20, err=FAKE, skip=FAKE):
     L = q.lib()
     arr = (q.nf4_layer * max(1, len(layers)))(*layers)
     if name == "nf4_layer_error":
         return L.nf4_layer_error(arr, len(layers), f, err, ws, ws_bytes, None)
+    if name == "nf4_dequantize_masked":
+        return L.nf4_dequantize_masked(arr, len(layers), f, skip, ws, ws_bytes, None)
     return getattr(L, name)(arr, len(layers), f, ws, ws_bytes, None)
 
 
-CODEC = ["nf4_quantize", "nf4_double_quant", "nf4_dequantize", "nf4_layer_error"]
+CODEC = ["nf4_quantize", "nf4_double_quant", "nf4_dequantize", "nf4_dequantize_masked", "nf4_layer_error"]
 
 
 @pytest.mark.parametrize("name", CODEC)
@@ -103,6 +105,7 @@ def test_bad_layers(name):
     need = {"nf4_quantize": ["w", "codes", "absmax", "qabsmax", "scale2"],
             "nf4_double_quant": ["absmax", "qabsmax", "scale2"],
             "nf4_dequantize": ["codes", "qabsmax", "scale2", "out"],
+            "nf4_dequantize_masked": ["codes", "qabsmax", "scale2", "out"],
             "nf4_layer_error": ["w", "codes", "qabsmax", "scale2"]}[name]
     for field in need:
         assert _call(name, [_L(**{field: None})], f) == q.NF4_E_ARG, field
@@ -113,8 +116,10 @@ def test_bad_layers(name):
         assert L.nf4_layer_error(arr, 1, f, FAKE + 4, FAKE, 1 << 20, None) == q.NF4_E_ALIGN
         # absmax optional with double quant, required without
         assert _call(name, [_L(absmax=None)], q.fmt(dq=False)) == q.NF4_E_ARG
-    if name == "nf4_dequantize":
+    if name in ("nf4_dequantize", "nf4_dequantize_masked"):
         assert _call(name, [_L(absmax=None)], q.fmt(dq=False)) == q.NF4_E_ARG
+    if name == "nf4_dequantize_masked":
+        assert _call(name, [_L()], f, skip=None) == q.NF4_E_ARG
 
 
 @pytest.mark.parametrize("name", CODEC)
@@ -142,6 +147,7 @@ def test_misaligned_pointers(name):
     fields = {"nf4_quantize": {"w": 16, "codes": 16, "absmax": 4, "scale2": 4},
               "nf4_double_quant": {"absmax": 4, "scale2": 4},
               "nf4_dequantize": {"codes": 16, "scale2": 4, "out": 16},
+              "nf4_dequantize_masked": {"codes": 16, "scale2": 4, "out": 16},
               "nf4_layer_error": {"w": 16, "codes": 16, "absmax": 4, "scale2": 4}}[name]
     for field, a in fields.items():
         for off in (1, 2, 4, a // 2) if a > 2 else (1,):
@@ -161,7 +167,8 @@ def test_workspace_checks(name):
     # quantise: table + tile records; fused pass: + error partials; dequantisation: table +
     # a 32-byte record per tile; double quant: table only
     small = {"nf4_quantize": tab_only + rec, "nf4_double_quant": tab_only,
-             "nf4_layer_error": tab_only + rec + part, "nf4_dequantize": tab_only + part}[name] - 1
+             "nf4_layer_error": tab_only + rec + part, "nf4_dequantize": tab_only + part,
+             "nf4_dequantize_masked": tab_only + part}[name] - 1
     assert _call(name, [_L(n=ns[0])], f, ws=None) == q.NF4_E_WORKSPACE
     assert _call(name, [_L(n=ns[0])], f, ws=FAKE + 64) == q.NF4_E_WORKSPACE
     assert _call(name, [_L(n=ns[0])], f, ws_bytes=small) == q.NF4_E_WORKSPACE

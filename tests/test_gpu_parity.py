@@ -14,7 +14,7 @@ import oracle
 import quantized_lora_fine_nf4_amd as q
 import synth
 from conftest import print_case
-from gpu_util import compare_layer, layer_error, layerset, np_of, poison, rel_err, workspace
+from gpu_util import POISON, compare_layer, layer_error, layerset, np_of, poison, rel_err, workspace
 from synth import configs
 
 pytestmark = pytest.mark.gpu
@@ -225,6 +225,44 @@ def test_toy_stack_end_to_end():
     for i in range(cfg.n_layers):
         if ref_sel[i]:   # promoted layers are not dequantised: output left untouched
             assert np.all(np_of(ls.out_of(i), np.uint8) == 0x5A)
+    # the same step with the selection left on the device: the selected array
+    # is the skip mask, no host round trip
+    ls.out.view(torch.uint8).fill_(0x5A)
+    q.nf4_dequantize_masked(ls, f, sel, workspace(ls.ns, f))
+    torch.cuda.synchronize()
+    for i in range(cfg.n_layers):
+        if ref_sel[i]:
+            assert np.all(np_of(ls.out_of(i), np.uint8) == 0x5A)
+        else:
+            assert np.array_equal(np_of(ls.out_of(i), np.uint16), refs[i]["y"])
+
+
+@pytest.mark.parametrize("dq", [False, True], ids=["nodq", "dq"])
+@pytest.mark.parametrize("dtname", ["bf16", "fp16"])
+def test_masked_dequantize_matches_oracle(dtname, dq):
+    """nf4_dequantize_masked on the edge layers (ragged sizes, zero, subnormal
+    and huge blocks): the layers with a zero mask byte equal the oracle's
+    dequantised values bit for bit, the others keep their poisoned output;
+    an all-zero mask equals nf4_dequantize, an all-one mask writes nothing."""
+    dtype = DTYPES[dtname]
+    f = q.fmt(dtype, dq)
+    layers = _edge_layers(dtype)
+    print_case("masked dequant", dtname, "dq" if dq else "nodq", len(layers))
+    ls = layerset([w for _, w in layers], f)
+    layer_error(ls, f)
+    ws = workspace(ls.ns, f)
+    nl = len(layers)
+    refs = [compare_layer(ls, i, w, dtype, dq) for i, (_, w) in enumerate(layers)]
+    for pattern in ([i % 2 for i in range(nl)], [1 - i % 2 for i in range(nl)], [0] * nl, [1] * nl):
+        skip = torch.tensor(pattern, dtype=torch.uint8, device="cuda")
+        ls.out.view(torch.uint8).fill_(POISON)
+        q.nf4_dequantize_masked(ls, f, skip, ws)
+        torch.cuda.synchronize()
+        for i in range(nl):
+            if pattern[i]:
+                assert np.all(np_of(ls.out_of(i), np.uint8) == POISON), (i, pattern)
+            else:
+                assert np.array_equal(np_of(ls.out_of(i), np.uint16), refs[i]["y"]), (i, pattern)
 
 
 def test_single_matrix_with_outliers():
