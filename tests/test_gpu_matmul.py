@@ -135,17 +135,18 @@ def test_matmul_fullsize_ffn_sampled(backward, dtype):
     print(f"[{'bwd' if backward else 'fwd'}] worst error / bound {worst:.3f}", flush=True)
 
 
+@pytest.mark.parametrize("dq", [True, False], ids=["dq", "nodq"])
 @pytest.mark.parametrize("m", [3300, 3100])
 @pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
-def test_matmul_tail_halves_match_oracle(backward, m):
+def test_matmul_tail_halves_match_oracle(backward, m, dq):
     """260 output tiles of 256 x 256 on 256 CUs: the 4 tiles past the whole
     round run in row pieces (128-row halves forward, 64-row quarters
     backward), some of them over the ragged last 228 or 28 rows and, at
     m = 3100, some entirely past the last row; every output element is
-    checked."""
+    checked, with double quant and with fp32 absmax."""
     rows, cols = (256, 5120) if backward else (5120, 256)
-    print_case("nf4_matmul tail halves", m, rows, cols, "bwd" if backward else "fwd")
-    W = DevWeight(rows, cols, 515, True, outliers=0.001)
+    print_case("nf4_matmul tail halves", m, rows, cols, "dq" if dq else "nodq", "bwd" if backward else "fwd")
+    W = DevWeight(rows, cols, 515, dq, outliers=0.001)
     xb = _x(m, rows if backward else cols, 516)
     out = _run(W, xb, backward)
     _check(out, xb, W, backward)
