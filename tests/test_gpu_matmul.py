@@ -121,8 +121,8 @@ def test_matmul_is_deterministic():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("backward,dtype", [(False, BF16), (True, BF16), (False, FP16)],
-                         ids=["fwd-bf16", "bwd-bf16", "fwd-fp16"])
+@pytest.mark.parametrize("backward,dtype", [(False, BF16), (True, BF16), (False, FP16), (True, FP16)],
+                         ids=["fwd-bf16", "bwd-bf16", "fwd-fp16", "bwd-fp16"])
 def test_matmul_fullsize_ffn_sampled(backward, dtype):
     rows, cols, m = 13824, 5120, 4096
     print_case("nf4_matmul full size", dtype, rows, cols, m, "bwd" if backward else "fwd")
