@@ -210,11 +210,11 @@ __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, 
 __device__ __forceinline__ uint32_t absmax_bits8_f16ops(const u32x4 v)
 {
     const h2 a = as_h2(v.x), b = as_h2(v.y), c = as_h2(v.z), d = as_h2(v.w);
-    const h2 mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
-                                                __builtin_elementwise_maximum(c, d));
-    const h2 mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b),
-                                                __builtin_elementwise_minimum(c, d));
-    const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(mx, -mn));
+    // chained so that each step is one three-operand instruction: max of
+    // a, b, c; min of a, b, c, then of d; then max(that max, d, -min)
+    const h2 mx3 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+    const h2 mn4 = __builtin_elementwise_minimum(__builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c), d);
+    const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx3, d), -mn4));
     const uint32_t lo = r & 0xffffu, hi = r >> 16;
     return lo > hi ? lo : hi;
 }
