@@ -275,6 +275,26 @@ def variants(q, torch, ls, f, err, cost, budget, cfg, stream, ws, fused_bytes, r
         "relative_mean": float(rel.mean()), "relative_min": float(rel.min()),
         "relative_max": float(rel.max())}
     res["nf4_layer_error_norm_GBps"] = round(fused_bytes / (t_norm * 1e-3) / 1e9, 1)
+    # the standalone calls of the boundary on the whole stack: nf4_quantize
+    # (absmax, codes and, with double quant, the second level; no error) on a
+    # set that shares the stack's weights and codes and adds the fp32 absmax it
+    # writes, then nf4_double_quant of those absmax values
+    qs = q.LayerSet(cfg.sizes, f, with_absmax=True, with_out=False, w=ls.w, codes=ls.codes)
+    qws = torch.empty(q.nf4_workspace_bytes(qs.ns, f), dtype=torch.uint8, device="cuda")
+    n_all = cfg.total
+    ngroups = sum((n + 16383) // 16384 for n in cfg.sizes)
+    t_q = timed(lambda: q.nf4_quantize(qs, f, qws))
+    qb = 2.5 * n_all + 4.0 * n_all / 64 + ((n_all / 64 + 4.0 * ngroups) if cfg.dq else 0.0)
+    res["nf4_quantize_ms"] = round(t_q, 4)
+    res["nf4_quantize_GBps"] = round(qb / (t_q * 1e-3) / 1e9, 1)
+    res["nf4_quantize_frac_of_peak"] = round(qb / (t_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if cfg.dq:
+        t_dq = timed(lambda: q.nf4_double_quant(qs, f, qws))
+        db = 4.0 * n_all / 64 + n_all / 64 + 4.0 * ngroups   # absmax read, int8 and scale2 written
+        res["nf4_double_quant_ms"] = round(t_dq, 4)
+        res["nf4_double_quant_GBps"] = round(db / (t_dq * 1e-3) / 1e9, 1)
+        res["nf4_double_quant_frac_of_peak"] = round(db / (t_dq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    del qs, qws
     m = len(cfg.per_block)
     ge = list(range(m, nl + 1, m))
     sws = torch.empty(q.aqlora_workspace_bytes(nl), dtype=torch.uint8, device="cuda")

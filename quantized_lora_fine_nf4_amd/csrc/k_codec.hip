@@ -2,13 +2,14 @@
 //
 // One tile = one double-quantisation group = 256 blocks of 64 weights
 // (16384 weights, 32 KB of bf16).  The tiles of all layers form one flat
-// index, so one grouped launch covers the whole stack.  The fused and
-// double-quant kernels are persistent: a 256-thread workgroup (4 waves) owns a
-// tile at a time; lane layout: wave w, load j (j = 0..7), lane L reads weights
+// index, so one grouped launch covers the whole stack.  The fused kernel is a
+// one-shot grid of one 256-thread workgroup (4 waves) per tile; lane layout:
+// wave w, load j (j = 0..7), lane L reads weights
 // w*4096 + j*512 + 8L .. +8 with one 128-bit load, so each load instruction of
 // a wave covers 1 KB contiguously and the 8 lanes 8m..8m+7 hold the 64 weights
-// of one block.  The standalone dequantisation is a one-shot grid of small
-// workgroups, each an eighth of a tile, reading a per-tile record (see there).
+// of one block.  The standalone double quantisation takes one wave per tile,
+// the standalone dequantisation one small workgroup per eighth of a tile
+// reading a per-tile record (see there); both are one-shot grids.
 //
 // What is computed (see nf4.h for the full format):
 //   absmax      -- "quantisation constants" per block ("QLoRA" paper summary
@@ -47,7 +48,6 @@ constexpr int kRepl = 8;
 constexpr int kYStride = 256 + 17;     // per-block dequant table, code-major, padded against bank conflicts
 constexpr int kCodecWavesPerEu = 4;    // register cap of the fused pass (5 fit: 91 VGPRs; LDS allows 5)
 constexpr int kQuantWavesPerEu = 3;    // the pass without the error (nf4_quantize): at 4 it spilled
-constexpr int kXcds = 8;             // accelerator dies (XCDs), each with its own L2 and translation caches
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 128-bit load / store unit
@@ -357,23 +357,6 @@ struct TileRef {
     int valid;       // elements of the tile inside the layer (1..16384)
 };
 
-// First tile of this workgroup in a persistent walk over the flat tile index;
-// every later tile is G = gridDim.x further on, so pass k covers tiles
-// [k G, (k+1) G).  Workgroups are handed to the XCDs round-robin by index, so
-// with the identity order each XCD would own every 8th tile of a pass and its
-// translation cache would have to map the whole pass.  Giving XCD x the
-// contiguous run x G/8 .. (x+1) G/8 - 1 of every pass shrinks the span each
-// XCD touches at once eightfold.  Only the order changes, so results do not
-// depend on it; a grid that is not a multiple of 8 keeps the identity order.
-// Both persistent kernels use it (the fused pass: 6.63 -> 6.57 ms on the 14B stack).
-template <bool XCD>
-__device__ __forceinline__ int64_t walk_start()
-{
-    const uint32_t b = blockIdx.x, g = gridDim.x;
-    if (!XCD || g % kXcds) return b;
-    return (int64_t)(b % kXcds) * (g / kXcds) + b / kXcds;
-}
-
 __device__ __forceinline__ int first_layer(const LayerDesc* tab, int nl, int64_t tile)
 {
     int lo = 0, hi = nl - 1;
@@ -450,7 +433,7 @@ __device__ void init_shared(CodecShared& sh)
 // finite and leaves the codes unchanged), and each difference is scaled by
 // 2^k before squaring so that the fp32 squares neither underflow nor
 // overflow (exact; undone in fp64 per block, counted once per 8-lane group).
-// FULL: a whole tile (the persistent kernel); otherwise a matrix's ragged
+// FULL: a whole tile (the one-shot kernel); otherwise a matrix's ragged
 // last tile (the tail kernel), whose codes past the end are 0 (an odd tail's
 // high nibble) and whose bytes past the end are not written.
 // NORM (with ERR): also the sum of x^2 over the lane's weights, in the same
@@ -1009,38 +992,46 @@ __global__ __launch_bounds__(kDqThreads) void k_dequant(const DqTile* __restrict
 
 // ---- standalone double quantisation --------------------------------------
 
+// One wave per double-quant group (256 blocks, a tile), four groups per
+// workgroup, a one-shot grid: lane L takes blocks L + 64 k (k = 0..3), so each
+// load and store instruction of the wave covers one contiguous run; the group
+// maximum is a wave maximum, with no workgroup barrier.  The arithmetic is
+// that of the fused pass's exact-division path: s2 = fl32(G / 127), q =
+// rint(fl32(a / s2)) clamped to +-127 (a <= G, so the clamp never applies).
+constexpr int kDqGroupsPerWg = kThreads / 64;
+
 __global__ __launch_bounds__(kThreads) void k_double_quant(const LayerDesc* __restrict__ tab,
                                                            int nl, int64_t ntiles)
 {
-    __shared__ uint32_t s_wmax[kWaves];
-    const int64_t start = walk_start<true>();
-    if (start >= ntiles) return;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    int l = first_layer(tab, nl, start);
-    for (int64_t tile = start; tile < ntiles; tile += gridDim.x) {
-        const TileRef tr = tile_ref(tab, l, tile);
-        const TileRef& d = tr;
-        const int nbv = (tr.valid + 63) >> 6;
-        const int64_t b = (tr.e0 >> 6) + t;
-        const float a = (t < nbv) ? ((g_cf32)d.absmax)[b] : 0.0f;
-        const uint32_t wm = wave_max_u32(as_u(a));
-        if (lane == 0) s_wmax[wv] = wm;
-        __syncthreads();
-        uint32_t g = s_wmax[0];
-        for (int i = 1; i < kWaves; ++i) g = max(g, s_wmax[i]);
-        __syncthreads();
-        const float G = as_f(g);
-        float s2 = 0.0f;
+    const int64_t tile = (int64_t)blockIdx.x * kDqGroupsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (tile >= ntiles) return;   // the whole wave
+    const int lane = threadIdx.x & 63;
+    int l = first_layer(tab, nl, tile);
+    const TileRef tr = tile_ref(tab, l, tile);
+    const int nbv = (tr.valid + 63) >> 6;
+    const int64_t b0 = tr.e0 >> 6;
+    float a[4];
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = lane + 64 * k;
+        a[k] = b < nbv ? ((g_cf32)tr.absmax)[b0 + b] : 0.0f;
+        m = max(m, as_u(a[k]));   // absmax >= 0: the integer order is the numeric order
+    }
+    const float G = as_f(wave_max_u32(m));
+    const float s2 = G > 0.0f ? G / 127.0f : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = lane + 64 * k;
         int8_t q = 0;
         if (G > 0.0f) {
-            s2 = G / 127.0f;
-            float qf = rintf(a / s2);
+            float qf = rintf(a[k] / s2);
             qf = fminf(fmaxf(qf, -127.0f), 127.0f);
             q = (int8_t)qf;
         }
-        if (t < nbv) ((g_i8)d.qabsmax)[b] = q;
-        if (t == 0) ((g_f32)d.scale2)[tr.local] = s2;
+        if (b < nbv) ((g_i8)tr.qabsmax)[b0 + b] = q;
     }
+    if (lane == 0) ((g_f32)tr.scale2)[tr.local] = s2;
 }
 
 // ---- per-layer reduction of the tile partials -----------------------------
@@ -1065,29 +1056,6 @@ __global__ __launch_bounds__(kThreads) void k_reduce(const LayerDesc* __restrict
 }
 
 // ---- launch helpers -------------------------------------------------------
-
-int cu_count()
-{
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
-}
-
-// Workgroups of a persistent launch: the resident count per CU (capped at
-// max_per_cu when given) times the CUs, at most one per tile.
-template <typename K>
-int64_t persistent_grid(K kernel, int64_t ntiles, int threads = kThreads, int max_per_cu = 0)
-{
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-        per_cu <= 0)
-        per_cu = 4;
-    if (max_per_cu > 0 && per_cu > max_per_cu) per_cu = max_per_cu;
-    const int64_t g = (int64_t)cu_count() * per_cu;
-    return ntiles < g ? ntiles : g;
-}
 
 // One-shot launches of at most kMaxGrid workgroups (the dispatch packet counts
 // work-items in 32 bits).
@@ -1172,7 +1140,8 @@ hipError_t launch_dequant(const LayerDesc* tab, int nl, int64_t ntiles, int dtyp
 
 hipError_t launch_double_quant(const LayerDesc* tab, int nl, int64_t ntiles, hipStream_t s)
 {
-    const int64_t grid = persistent_grid(k_double_quant, ntiles);
+    const int64_t grid = (ntiles + kDqGroupsPerWg - 1) / kDqGroupsPerWg;
+    if (grid > kMaxGrid) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_double_quant, dim3((unsigned)grid), dim3(kThreads), 0, s, tab, nl, ntiles);
     return hipGetLastError();
 }
